@@ -1,0 +1,147 @@
+/* ckks_ks.h - RNS-CKKS hybrid key-switching on one AMD Instinct MI355X (gfx950).
+ *
+ * The method: half of every key-switching key is uniformly random, so instead
+ * of being stored it can be regenerated inside the kernels that use the key by a
+ * counter-mode ChaCha12 expander, halving key storage; the chain is an RNS CKKS
+ * chain of 32-bit primes (Perseus summary on ai4snews, "Interpretation"
+ * paragraph 2; the Perseus abstract names this in-kernel key regeneration as its
+ * backend-level change).  The rest of the path is textbook hybrid key-switching
+ * (Han and Ki, CT-RSA 2020) with fast base conversion (Bajard et al., SAC 2016)
+ * and merged-twist negacyclic NTTs (Longa and Naehrig 2016).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked (host).  Every residue array is
+ *    uint32_t, limb-major: [.. ][limb][N], coefficient n of limb i at i*N + n.
+ *  - Residues are canonical, in [0, q), on input and output.  Polynomials are in
+ *    the NTT domain (bit-reversed evaluation order: entry j holds the value at
+ *    psi^(2*brv(j)+1), psi the smallest primitive 2N-th root mod q) except the
+ *    output of ckks_ntt_inv and the input of ckks_ntt_fwd.
+ *  - The chain is q_0..q_{L-1} (ciphertext primes) then p_0..p_{K-1} (special
+ *    primes); absolute prime index t runs over all L+K.  Level l means the
+ *    ciphertext primes q_0..q_{l-1} are active.  Digit width alpha = ceil(L/dnum);
+ *    digit j at level l holds primes j*alpha .. min((j+1)*alpha, l)-1 and there
+ *    are d_l = ceil(l/alpha) digits.
+ *  - Keys: key_b and key_a are [dnum][L+K][N], row (j, t) for digit j and
+ *    absolute prime t, so one key serves every level.  The a-half is exactly the
+ *    ChaCha12 expansion of the key's 32-byte seed (see ckks_expand_a).
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the default stream) and never synchronises the host.  Calls on one
+ *    context share its workspace: calls on different streams must not overlap
+ *    (use one context per stream).  Output buffers must not alias inputs.
+ *  - Arguments are validated before anything is launched; on failure nothing is
+ *    launched and the status says why (ckks_last_error() holds a message for the
+ *    calling thread).  The library never allocates device memory outside
+ *    ckks_ctx_create.
+ */
+#ifndef CKKS_KS_H
+#define CKKS_KS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ckks_ctx ckks_ctx;
+
+typedef enum {
+  CKKS_OK = 0,
+  CKKS_EINVAL = -1,        /* NULL pointer, bad enum, inconsistent sizes */
+  CKKS_ERANGE = -2,        /* level, batch, Galois element or prime out of range */
+  CKKS_ENOMEM = -3,        /* device allocation failed in ckks_ctx_create */
+  CKKS_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  CKKS_EUNSUPPORTED = -5   /* parameters this build does not implement */
+} ckks_status;
+
+/* Thread-local description of the last failure on the calling thread ("" if none). */
+const char *ckks_last_error(void);
+
+/* The `count` largest primes q < 2^bits with q = 1 mod 2^(log_n+1), in descending
+ * order, written to out_host[0..count) (host).  This is the chain reading used
+ * throughout: the pages fix only "a 32-bit RNS CKKS chain".  bits in 20..32. */
+ckks_status ckks_chain_primes(uint32_t log_n, uint32_t bits, uint32_t count, uint32_t *out_host);
+
+/* Create a context for ring degree N = 2^log_n (12 <= log_n <= 16), chain
+ * primes[0..num_q+num_p) (host; ciphertext primes first), dnum digits, and a
+ * workspace for up to max_batch ciphertexts (or hoisted keys) per call at level
+ * num_q.  Every prime must be prime, < 2^32, = 1 mod 2N, and all distinct;
+ * num_p >= ceil(num_q/dnum) is required (the special modulus covers a digit).
+ * max_batch = 0 creates a host-only context: every table is computed and every
+ * argument check works, but no HIP call is made and compute calls return
+ * CKKS_EINVAL.  Errors: EINVAL (NULL), ERANGE (sizes, non-qualifying prime),
+ * EUNSUPPORTED (log_n outside 12..16), ENOMEM/EHIP (device setup). */
+ckks_status ckks_ctx_create(ckks_ctx **out, uint32_t log_n, uint32_t num_q, uint32_t num_p,
+                            uint32_t dnum, const uint32_t *primes, uint32_t max_batch);
+void ckks_ctx_destroy(ckks_ctx *ctx);
+
+/* Host copies of what the context derived: the minimal 2N-th root psi_t of every
+ * prime (roots_out[L+K]) and the context's sizes. Any output pointer may be NULL. */
+ckks_status ckks_ctx_info(const ckks_ctx *ctx, uint32_t *n_out, uint32_t *num_q_out, uint32_t *num_p_out,
+                          uint32_t *dnum_out, uint32_t *alpha_out, uint32_t *max_batch_out,
+                          uint64_t *workspace_bytes_out, uint32_t *roots_out);
+
+/* Forward negacyclic NTT, in place, of data[batch][n_limbs][N] (coefficients in
+ * natural order in, NTT domain out); limb i of each item is taken modulo chain
+ * prime first_prime + i.  Errors: ERANGE if first_prime + n_limbs > L+K or batch
+ * or n_limbs is 0. */
+ckks_status ckks_ntt_fwd(const ckks_ctx *ctx, uint32_t *data, uint32_t first_prime, uint32_t n_limbs,
+                         uint32_t batch, void *stream);
+/* Inverse of ckks_ntt_fwd (includes the factor N^-1). */
+ckks_status ckks_ntt_inv(const ckks_ctx *ctx, uint32_t *data, uint32_t first_prime, uint32_t n_limbs,
+                         uint32_t batch, void *stream);
+
+/* ModUp: extended digits of c1[batch][level][N] (NTT domain).  digits is
+ * [batch][d_l][level+K][N]: limb e of digit j is over prime e (e < level) or
+ * p_{e-level}; for a prime of digit j it is c1's own limb, otherwise the NTT of
+ * the fast base conversion of digit j's coefficients, without overflow
+ * correction.  Errors: ERANGE for level outside 1..L or batch outside 1..max_batch. */
+ckks_status ckks_modup(const ckks_ctx *ctx, const uint32_t *c1, uint32_t level, uint32_t *digits,
+                       uint32_t batch, void *stream);
+
+/* ModDown: out[batch][level][N] = (x_i - NTT(conv_{P->q_i}(INTT(x_P)))) * P^-1 mod q_i for
+ * x[batch][level+K][N] (level ciphertext limbs then K special limbs, NTT domain);
+ * floor-type: no P/2 offset, conversion overflow left in.  Errors as ckks_modup. */
+ckks_status ckks_moddown(const ckks_ctx *ctx, const uint32_t *x, uint32_t level, uint32_t *out,
+                         uint32_t batch, void *stream);
+
+/* Key-switch of ct[batch][2][level][N] (c0 then c1) under one key with Galois
+ * element galois_elt (odd, < 2N; 1 = no automorphism):
+ *   out = (sigma(c0) + ModDown(sum_j sigma(d_j) * b_j), ModDown(sum_j sigma(d_j) * a_j))
+ * with d_j the ModUp digits of c1 and sigma applied in the NTT domain after ModUp.
+ * key_a == NULL: the a-half is regenerated in-kernel from key_seed (host, 32
+ * bytes); otherwise key_a is the stored a-half and key_seed is ignored (may be
+ * NULL).  Errors: EINVAL (NULL ct/key_b/out, or both key_a and key_seed NULL),
+ * ERANGE (level, batch, even or out-of-range galois_elt). */
+ckks_status ckks_keyswitch(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, const uint32_t *key_b,
+                           const uint8_t *key_seed, const uint32_t *key_a, uint32_t galois_elt,
+                           uint32_t *out, uint32_t batch, void *stream);
+
+/* Hoisted key-switch: one ModUp of ct[2][level][N], then for every key k an
+ * inner product and ModDown with (key_b[k], key_a[k] or key_seeds[k], galois_elts[k]);
+ * out is [n_keys][2][level][N], bit-identical to n_keys calls of ckks_keyswitch.
+ * key_b, galois_elts and key_seeds are host arrays (key_b holds device
+ * pointers; key_seeds is 32*n_keys bytes); key_a is NULL (all regenerated) or a
+ * host array of device pointers whose NULL entries are regenerated.
+ * 1 <= n_keys <= 64.  Errors as ckks_keyswitch. */
+ckks_status ckks_keyswitch_hoisted(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, uint32_t n_keys,
+                                   const uint32_t *const *key_b, const uint8_t *key_seeds,
+                                   const uint32_t *const *key_a, const uint32_t *galois_elts,
+                                   uint32_t *out, void *stream);
+
+/* The a-half [dnum][L+K][N] that key_seed (host, 32 bytes) regenerates: the stored
+ * variant of a key.  Stream layout: one ChaCha12 sub-stream per (digit j,
+ * absolute prime t, tile tau of 1024 coefficients); state = "expand 32-byte k",
+ * the seed as 8 little-endian words, block counter from 0, then j, t, tau; words
+ * in counter then word order; a word w is accepted iff w < floor(2^32/q_t)*q_t
+ * and gives w mod q_t; the k-th accepted word is coefficient tau*1024 + k. */
+ckks_status ckks_expand_a(const ckks_ctx *ctx, const uint8_t *key_seed, uint32_t *key_a, void *stream);
+
+/* Test knob: number of ChaCha blocks generated per 1024-word tile before the
+ * rare continuation path runs (default 68, at least 64).  64 sends every tile
+ * with a rejected word through the continuation path. */
+ckks_status ckks_ctx_set_regen_blocks(ckks_ctx *ctx, uint32_t blocks);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CKKS_KS_H */

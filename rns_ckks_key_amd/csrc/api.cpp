@@ -1,0 +1,725 @@
+// C-ABI of the key-switching library: argument checks, host precompute of the
+// constant tables, device workspace, and the launch sequence of each call.
+//
+// Launch sequence of one key-switch of `batch` ciphertexts at level l (all on
+// the caller's stream, no host synchronisation):
+//   1. k_row  (inverse)   c1 -> rowtmp           row half of INTT(c1)
+//   2. k_conv (ModUp)     rowtmp -> ext          column INTT, scale, conversion, column NTT
+//   3. k_ip   (special)   ext, key -> tmpP       row NTT, sigma_g, inner product, row INTT
+//   4. k_conv (ModDown)   tmpP -> conv           column INTT, scale, P->Q conversion, column NTT
+//   5. k_ip   (final)     ext, c1, c0, conv, key -> out
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ckks_ks.h"
+#include "ckks_internal.h"
+
+using ckks::DevTables;
+
+namespace {
+
+thread_local std::string g_err;
+
+ckks_status fail(ckks_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ckks_status fail(ckks_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ckks_status ok() {
+  g_err.clear();
+  return CKKS_OK;
+}
+
+// ---------------------------------------------------------------- number theory (host)
+
+uint32_t mulmod(uint32_t a, uint32_t b, uint32_t m) { return (uint32_t)((uint64_t)a * b % m); }
+
+uint32_t powmod(uint32_t b, uint64_t e, uint32_t m) {
+  uint64_t r = 1 % m, x = b % m;
+  while (e) {
+    if (e & 1) r = r * x % m;
+    x = x * x % m;
+    e >>= 1;
+  }
+  return (uint32_t)r;
+}
+
+uint32_t invmod(uint32_t a, uint32_t p) { return powmod(a, p - 2, p); }  // p prime
+
+// Deterministic Miller-Rabin for n < 2^32 with bases 2, 7, 61.
+bool is_prime32(uint32_t n) {
+  if (n < 2) return false;
+  for (uint32_t p : {2u, 3u, 5u, 7u, 11u, 13u, 61u})
+    if (n % p == 0) return n == p;
+  uint32_t d = n - 1, s = 0;
+  while (!(d & 1)) { d >>= 1; ++s; }
+  for (uint32_t a : {2u, 7u, 61u}) {
+    uint64_t x = powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool comp = true;
+    for (uint32_t r = 1; r < s; ++r) {
+      x = x * x % n;
+      if (x == n - 1) { comp = false; break; }
+    }
+    if (comp) return false;
+  }
+  return true;
+}
+
+// Smallest x with x^n = -1 mod q: the minimum over all primitive 2n-th roots (odd powers of one).
+uint32_t min_root(uint32_t q, uint32_t n) {
+  uint32_t w = 0;
+  for (uint32_t h = 2;; ++h) {
+    w = powmod(h, (q - 1) / (2 * (uint64_t)n), q);
+    if (powmod(w, n, q) == q - 1) break;
+  }
+  const uint32_t w2 = mulmod(w, w, q);
+  uint32_t best = w, x = w;
+  for (uint32_t k = 1; k < n; ++k) {
+    x = mulmod(x, w2, q);
+    best = std::min(best, x);
+  }
+  return best;
+}
+
+uint32_t brv(uint32_t x, uint32_t bits) {
+  uint32_t r = 0;
+  for (uint32_t i = 0; i < bits; ++i) { r = (r << 1) | (x & 1); x >>= 1; }
+  return r;
+}
+
+uint32_t inv2_32(uint32_t q) {  // q^-1 mod 2^32 by Newton iteration
+  uint32_t x = q;
+  for (int i = 0; i < 5; ++i) x *= 2 - q * x;
+  return x;
+}
+
+uint2 mont(uint32_t w, uint32_t q) {  // (w*2^32 mod q, companion)
+  uint32_t wm = (uint32_t)(((uint64_t)(w % q) << 32) % q);
+  return make_uint2(wm, wm * inv2_32(q));
+}
+
+uint32_t r64(uint32_t q) {  // 2^64 mod q
+  uint32_t r32 = (uint32_t)((1ull << 32) % q);
+  return mulmod(r32, r32, q);
+}
+
+struct Host {
+  uint32_t log_n = 0, n = 0, L = 0, K = 0, dnum = 0, alpha = 0;
+  std::vector<uint32_t> q, qinv, psi;
+  std::vector<uint2> tw, itw, ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one;
+  std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound;
+};
+
+void build_tables(Host& h) {
+  const uint32_t n = h.n, E = h.L + h.K, L = h.L, K = h.K, A = h.alpha;
+  h.qinv.resize(E);
+  h.psi.resize(E);
+  h.tw.resize((size_t)E * n);
+  h.itw.resize((size_t)E * n);
+  h.ninv.resize(E);
+  h.bound.resize(E);
+  h.one.resize(E);
+  for (uint32_t t = 0; t < E; ++t) {
+    const uint32_t q = h.q[t];
+    h.qinv[t] = inv2_32(q);
+    h.psi[t] = min_root(q, n);
+    const uint32_t pinv = invmod(h.psi[t], q);
+    std::vector<uint32_t> pw(n), ipw(n);
+    pw[0] = ipw[0] = 1;
+    for (uint32_t k = 1; k < n; ++k) {
+      pw[k] = mulmod(pw[k - 1], h.psi[t], q);
+      ipw[k] = mulmod(ipw[k - 1], pinv, q);
+    }
+    for (uint32_t k = 0; k < n; ++k) {
+      const uint32_t r = brv(k, h.log_n);
+      h.tw[(size_t)t * n + k] = mont(pw[r], q);
+      h.itw[(size_t)t * n + k] = mont(ipw[r], q);
+    }
+    h.ninv[t] = mont(invmod(n % q, q), q);
+    h.bound[t] = (uint32_t)(((1ull << 32) / q) * q);
+    h.one[t] = mont(1, q);
+  }
+  // ModUp: per level l, digit j, source prime i of the digit, target prime t
+  h.mu_scale.assign((size_t)(L + 1) * L, make_uint2(0, 0));
+  h.mu_conv.assign((size_t)(L + 1) * h.dnum * A * E, 0);
+  for (uint32_t l = 1; l <= L; ++l) {
+    const uint32_t d = (l + A - 1) / A;
+    for (uint32_t j = 0; j < d; ++j) {
+      const uint32_t lo = j * A, hi = std::min(lo + A, l);
+      for (uint32_t i = lo; i < hi; ++i) {
+        // [Qd/q_i]_{q_i} and its inverse, times N^-1
+        uint32_t qh = 1;
+        for (uint32_t i2 = lo; i2 < hi; ++i2)
+          if (i2 != i) qh = mulmod(qh, h.q[i2] % h.q[i], h.q[i]);
+        const uint32_t sc = mulmod(invmod(qh, h.q[i]), invmod(n % h.q[i], h.q[i]), h.q[i]);
+        h.mu_scale[(size_t)l * L + i] = mont(sc, h.q[i]);
+        for (uint32_t t = 0; t < E; ++t) {
+          const uint32_t qt = h.q[t];
+          uint32_t v = 1;
+          for (uint32_t i2 = lo; i2 < hi; ++i2)
+            if (i2 != i) v = mulmod(v, h.q[i2] % qt, qt);
+          h.mu_conv[(((size_t)l * h.dnum + j) * A + (i - lo)) * E + t] = mulmod(v, r64(qt), qt);
+        }
+      }
+    }
+  }
+  // ModDown
+  h.md_scale_ks.resize(K);
+  h.md_scale_pl.resize(K);
+  h.md_conv.resize((size_t)K * L);
+  h.md_conv64.resize((size_t)K * L);
+  h.md_fin_ks.resize(L);
+  h.md_fin_pl.resize(L);
+  for (uint32_t k = 0; k < K; ++k) {
+    const uint32_t pk = h.q[L + k];
+    uint32_t ph = 1;
+    for (uint32_t k2 = 0; k2 < K; ++k2)
+      if (k2 != k) ph = mulmod(ph, h.q[L + k2] % pk, pk);
+    const uint32_t base = mulmod(invmod(ph, pk), invmod(n % pk, pk), pk);
+    h.md_scale_pl[k] = mont(base, pk);
+    h.md_scale_ks[k] = mont(mulmod(base, r64(pk), pk), pk);
+    for (uint32_t i = 0; i < L; ++i) {
+      const uint32_t qi = h.q[i];
+      uint32_t v = 1;
+      for (uint32_t k2 = 0; k2 < K; ++k2)
+        if (k2 != k) v = mulmod(v, h.q[L + k2] % qi, qi);
+      h.md_conv[(size_t)k * L + i] = v;
+      h.md_conv64[(size_t)k * L + i] = mulmod(v, r64(qi), qi);
+    }
+  }
+  for (uint32_t i = 0; i < L; ++i) {
+    const uint32_t qi = h.q[i];
+    uint32_t p = 1;
+    for (uint32_t k = 0; k < K; ++k) p = mulmod(p, h.q[L + k] % qi, qi);
+    const uint32_t pinv = invmod(p, qi);
+    h.md_fin_pl[i] = mont(pinv, qi);
+    h.md_fin_ks[i] = mont(mulmod(pinv, r64(qi), qi), qi);
+  }
+}
+
+}  // namespace
+
+struct ckks_ctx {
+  Host h;
+  DevTables d{};
+  void* dev_tables = nullptr;
+  uint32_t max_batch = 0;
+  int device = -1;
+  uint32_t regen_blocks = ckks::kDefaultRegenBlocks;
+  // workspace (items = max_batch)
+  void* ws = nullptr;
+  uint64_t ws_bytes = 0;
+  uint32_t* rowtmp = nullptr;  // [B][max(L,K)][N]
+  uint32_t* ext = nullptr;     // [B][dnum][L+K][N]
+  uint32_t* tmpP = nullptr;    // [B][2][K][N]
+  uint32_t* conv = nullptr;    // [B][2][L][N]
+};
+
+namespace {
+
+template <typename T>
+size_t bytes_of(const std::vector<T>& v) { return v.size() * sizeof(T); }
+
+ckks_status upload_tables(ckks_ctx* c) {
+  Host& h = c->h;
+  struct Part { const void* src; size_t bytes; const void** dst; };
+  DevTables& d = c->d;
+  std::vector<Part> parts = {
+      {h.q.data(), bytes_of(h.q), (const void**)&d.q},
+      {h.qinv.data(), bytes_of(h.qinv), (const void**)&d.qinv},
+      {h.tw.data(), bytes_of(h.tw), (const void**)&d.tw},
+      {h.itw.data(), bytes_of(h.itw), (const void**)&d.itw},
+      {h.ninv.data(), bytes_of(h.ninv), (const void**)&d.ninv},
+      {h.mu_scale.data(), bytes_of(h.mu_scale), (const void**)&d.mu_scale},
+      {h.mu_conv.data(), bytes_of(h.mu_conv), (const void**)&d.mu_conv},
+      {h.md_scale_ks.data(), bytes_of(h.md_scale_ks), (const void**)&d.md_scale_ks},
+      {h.md_scale_pl.data(), bytes_of(h.md_scale_pl), (const void**)&d.md_scale_pl},
+      {h.md_conv.data(), bytes_of(h.md_conv), (const void**)&d.md_conv},
+      {h.md_conv64.data(), bytes_of(h.md_conv64), (const void**)&d.md_conv64},
+      {h.md_fin_ks.data(), bytes_of(h.md_fin_ks), (const void**)&d.md_fin_ks},
+      {h.md_fin_pl.data(), bytes_of(h.md_fin_pl), (const void**)&d.md_fin_pl},
+      {h.bound.data(), bytes_of(h.bound), (const void**)&d.bound},
+      {h.one.data(), bytes_of(h.one), (const void**)&d.one},
+  };
+  size_t total = 0;
+  for (auto& p : parts) total += (p.bytes + 255) & ~size_t(255);
+  if (hipMalloc(&c->dev_tables, total) != hipSuccess)
+    return fail(CKKS_ENOMEM, "hipMalloc of %zu bytes of constant tables failed", total);
+  size_t off = 0;
+  for (auto& p : parts) {
+    char* dst = (char*)c->dev_tables + off;
+    if (hipMemcpy(dst, p.src, p.bytes, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(CKKS_EHIP, "hipMemcpy of constant tables failed");
+    *p.dst = dst;
+    off += (p.bytes + 255) & ~size_t(255);
+  }
+  return CKKS_OK;
+}
+
+ckks_status check_ctx(const ckks_ctx* c) {
+  if (!c) return fail(CKKS_EINVAL, "ctx is NULL");
+  return CKKS_OK;
+}
+
+// Last check of every compute call, after all argument checks: a host-only context stops here.
+ckks_status check_device(const ckks_ctx* c) {
+  if (c->max_batch == 0) return fail(CKKS_EINVAL, "host-only context (max_batch = 0) cannot run device calls");
+  return CKKS_OK;
+}
+
+ckks_status check_level(const ckks_ctx* c, uint32_t level) {
+  if (level < 1 || level > c->h.L) return fail(CKKS_ERANGE, "level %u outside 1..%u", level, c->h.L);
+  return CKKS_OK;
+}
+
+ckks_status check_batch(const ckks_ctx* c, uint32_t batch) {
+  const uint32_t lim = c->max_batch ? c->max_batch : 4096;  // host-only contexts check the shape only
+  if (batch < 1 || batch > lim) return fail(CKKS_ERANGE, "batch %u outside 1..%u (context max_batch)", batch, lim);
+  return CKKS_OK;
+}
+
+ckks_status check_galois(const ckks_ctx* c, uint32_t g) {
+  if (g % 2 == 0 || g >= 2 * c->h.n)
+    return fail(CKKS_ERANGE, "Galois element %u must be odd and below 2N = %u", g, 2 * c->h.n);
+  return CKKS_OK;
+}
+
+ckks_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CKKS_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+void seed_words(const uint8_t* seed, uint32_t out[8]) {
+  for (int i = 0; i < 8; ++i)
+    out[i] = (uint32_t)seed[4 * i] | ((uint32_t)seed[4 * i + 1] << 8) | ((uint32_t)seed[4 * i + 2] << 16) |
+             ((uint32_t)seed[4 * i + 3] << 24);
+}
+
+uint32_t digits_at(const Host& h, uint32_t level) { return (level + h.alpha - 1) / h.alpha; }
+
+// Steps 1-2: INTT row half of c1 and the fused ModUp conversion into ctx->ext.
+hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, uint32_t level, uint32_t items,
+                     hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  ckks::RowArgs r{};
+  r.src = c1;
+  r.dst = c->rowtmp;
+  r.src_item_stride = c1_item_stride;
+  r.dst_item_stride = (uint64_t)level * N;
+  r.prime0 = 0;
+  r.n_limbs = level;
+  r.own_lo = r.own_n = 0;
+  r.level = 0;
+  hipError_t e = ckks::launch_row(c->d, r, false, items, s);
+  if (e != hipSuccess) return e;
+  ckks::ConvArgs a{};
+  a.src = c->rowtmp;
+  a.src_item = (uint64_t)level * N;
+  a.src_y = (uint64_t)h.alpha * N;
+  a.dst = c->ext;
+  a.dst_item = (uint64_t)h.dnum * (h.L + h.K) * N;
+  a.dst_y = (uint64_t)(h.L + h.K) * N;
+  a.src_prime0 = 0;
+  a.src_prime_step = h.alpha;
+  a.ns_max = h.alpha;
+  a.ns_limit = level;
+  a.scale = c->d.mu_scale + (size_t)level * h.L;
+  a.scale_y = h.alpha;
+  a.conv = c->d.mu_conv + (size_t)level * h.dnum * h.alpha * (h.L + h.K);
+  a.conv_y = h.alpha * (h.L + h.K);
+  a.conv_s = h.L + h.K;
+  a.conv_by_abs = 1;
+  a.skip = 1;
+  a.level = level;
+  a.n_targets = 0;  // per digit: level + K - (digit size), computed in the kernel
+  return ckks::launch_conv(c->d, a, digits_at(h, level), items, s);
+  return hipSuccess;
+}
+
+// Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (ctx->ext already filled).
+hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
+                          uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
+                          hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  ckks::IpArgs ip{};
+  ip.level = level;
+  ip.nd = digits_at(h, level);
+  ip.n_ct = n_ct;
+  ip.ext = c->ext;
+  ip.ext_ct_stride = ext_stride;
+  ip.ct = ct;
+  ip.ct_ct_stride = ct_stride;
+  ip.tmpP = c->tmpP;
+  ip.conv = c->conv;
+  ip.out = out;
+  ip.regen_blocks = c->regen_blocks;
+  ip.n_keys = n_keys;
+  for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
+  hipError_t e = ckks::launch_ip(c->d, ip, false, h.K, s);
+  if (e != hipSuccess) return e;
+  ckks::ConvArgs a{};
+  a.src = c->tmpP;
+  a.src_item = 2ull * h.K * N;
+  a.src_y = (uint64_t)h.K * N;
+  a.dst = c->conv;
+  a.dst_item = 2ull * level * N;
+  a.dst_y = (uint64_t)level * N;
+  a.src_prime0 = h.L;
+  a.src_prime_step = 0;
+  a.ns_max = h.K;
+  a.ns_limit = h.K;
+  a.scale = c->d.md_scale_ks;
+  a.scale_y = 0;
+  a.conv = c->d.md_conv;
+  a.conv_y = 0;
+  a.conv_s = h.L;
+  a.conv_by_abs = 0;
+  a.n_targets = level;
+  a.skip = 0;
+  a.level = level;
+  e = ckks::launch_conv(c->d, a, 2, n_ct * n_keys, s);
+  if (e != hipSuccess) return e;
+  return ckks::launch_ip(c->d, ip, true, level, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ckks_last_error(void) { return g_err.c_str(); }
+
+ckks_status ckks_chain_primes(uint32_t log_n, uint32_t bits, uint32_t count, uint32_t* out_host) {
+  if (!out_host) return fail(CKKS_EINVAL, "out_host is NULL");
+  if (bits < 20 || bits > 32) return fail(CKKS_ERANGE, "bits %u outside 20..32", bits);
+  if (log_n < 1 || log_n + 1 >= bits) return fail(CKKS_ERANGE, "log_n %u out of range for %u-bit primes", log_n, bits);
+  const uint64_t step = 2ull << log_n;
+  uint64_t cand = (1ull << bits) - step + 1;
+  uint32_t found = 0;
+  while (found < count) {
+    if (cand <= step) return fail(CKKS_ERANGE, "fewer than %u qualifying primes below 2^%u", count, bits);
+    if (is_prime32((uint32_t)cand)) out_host[found++] = (uint32_t)cand;
+    cand -= step;
+  }
+  return ok();
+}
+
+ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint32_t num_p, uint32_t dnum,
+                            const uint32_t* primes, uint32_t max_batch) {
+  if (!out) return fail(CKKS_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!primes) return fail(CKKS_EINVAL, "primes is NULL");
+  if (log_n < 12 || log_n > 16) return fail(CKKS_EUNSUPPORTED, "log_n %u: this build implements 12..16", log_n);
+  if (num_q < 1 || num_p < 1 || num_q + num_p > 256) return fail(CKKS_ERANGE, "num_q %u / num_p %u out of range", num_q, num_p);
+  if (dnum < 1 || dnum > ckks::kMaxDnum || dnum > num_q) return fail(CKKS_ERANGE, "dnum %u outside 1..min(%u, num_q)", dnum, ckks::kMaxDnum);
+  const uint32_t alpha = (num_q + dnum - 1) / dnum;
+  if (num_p < alpha) return fail(CKKS_ERANGE, "num_p %u below the digit width %u", num_p, alpha);
+  if (alpha > 24 || num_p > 24) return fail(CKKS_EUNSUPPORTED, "digit width %u / num_p %u above 24", alpha, num_p);
+  const uint32_t n = 1u << log_n;
+  for (uint32_t t = 0; t < num_q + num_p; ++t) {
+    const uint32_t q = primes[t];
+    if (q % (2 * n) != 1 || !is_prime32(q))
+      return fail(CKKS_ERANGE, "primes[%u] = %u is not a prime = 1 mod 2N", t, q);
+    for (uint32_t u = 0; u < t; ++u)
+      if (primes[u] == q) return fail(CKKS_ERANGE, "primes[%u] repeats primes[%u]", t, u);
+  }
+  if (max_batch > 4096) return fail(CKKS_ERANGE, "max_batch %u above 4096", max_batch);
+  ckks_ctx* c = new ckks_ctx();
+  Host& h = c->h;
+  h.log_n = log_n;
+  h.n = n;
+  h.L = num_q;
+  h.K = num_p;
+  h.dnum = dnum;
+  h.alpha = alpha;
+  h.q.assign(primes, primes + num_q + num_p);
+  build_tables(h);
+  c->max_batch = max_batch;
+  c->d.log_n = log_n;
+  c->d.n = n;
+  c->d.L = num_q;
+  c->d.K = num_p;
+  c->d.dnum = dnum;
+  c->d.alpha = alpha;
+  if (max_batch == 0) {
+    *out = c;
+    return ok();
+  }
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return fail(CKKS_EHIP, "hipGetDevice failed (no GPU?)");
+  }
+  ckks_status st = upload_tables(c);
+  if (st != CKKS_OK) {
+    std::string msg = g_err;
+    ckks_ctx_destroy(c);
+    g_err = msg;
+    return st;
+  }
+  const uint64_t N = n, E = num_q + num_p, B = max_batch;
+  const uint64_t rowtmp = B * std::max(num_q, num_p) * N, ext = B * dnum * E * N, tmpP = B * 2 * num_p * N,
+                 conv = B * 2 * num_q * N;
+  c->ws_bytes = (rowtmp + ext + tmpP + conv) * sizeof(uint32_t);
+  if (hipMalloc(&c->ws, c->ws_bytes) != hipSuccess) {
+    uint64_t b = c->ws_bytes;
+    ckks_ctx_destroy(c);
+    return fail(CKKS_ENOMEM, "hipMalloc of %llu workspace bytes failed", (unsigned long long)b);
+  }
+  c->rowtmp = (uint32_t*)c->ws;
+  c->ext = c->rowtmp + rowtmp;
+  c->tmpP = c->ext + ext;
+  c->conv = c->tmpP + tmpP;
+  *out = c;
+  return ok();
+}
+
+void ckks_ctx_destroy(ckks_ctx* c) {
+  if (!c) return;
+  if (c->ws) (void)hipFree(c->ws);
+  if (c->dev_tables) (void)hipFree(c->dev_tables);
+  delete c;
+}
+
+ckks_status ckks_ctx_info(const ckks_ctx* c, uint32_t* n_out, uint32_t* num_q_out, uint32_t* num_p_out,
+                          uint32_t* dnum_out, uint32_t* alpha_out, uint32_t* max_batch_out,
+                          uint64_t* workspace_bytes_out, uint32_t* roots_out) {
+  if (!c) return fail(CKKS_EINVAL, "ctx is NULL");
+  if (n_out) *n_out = c->h.n;
+  if (num_q_out) *num_q_out = c->h.L;
+  if (num_p_out) *num_p_out = c->h.K;
+  if (dnum_out) *dnum_out = c->h.dnum;
+  if (alpha_out) *alpha_out = c->h.alpha;
+  if (max_batch_out) *max_batch_out = c->max_batch;
+  if (workspace_bytes_out) *workspace_bytes_out = c->ws_bytes;
+  if (roots_out) std::copy(c->h.psi.begin(), c->h.psi.end(), roots_out);
+  return ok();
+}
+
+ckks_status ckks_ctx_set_regen_blocks(ckks_ctx* c, uint32_t blocks) {
+  if (!c) return fail(CKKS_EINVAL, "ctx is NULL");
+  if (blocks < ckks::kRow / 16 || blocks > ckks::kMaxRegenBlocks)
+    return fail(CKKS_ERANGE, "regen blocks %u outside %u..%u", blocks, ckks::kRow / 16, ckks::kMaxRegenBlocks);
+  c->regen_blocks = blocks;
+  return ok();
+}
+
+static ckks_status ntt_common(const ckks_ctx* c, uint32_t* data, uint32_t first, uint32_t n_limbs, uint32_t batch) {
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!data) return fail(CKKS_EINVAL, "data is NULL");
+  if (n_limbs == 0 || batch == 0) return fail(CKKS_ERANGE, "n_limbs and batch must be positive");
+  if ((uint64_t)first + n_limbs > c->h.L + c->h.K)
+    return fail(CKKS_ERANGE, "limbs %u..%u beyond the chain of %u primes", first, first + n_limbs - 1, c->h.L + c->h.K);
+  if (batch > 65535 || n_limbs > 65535) return fail(CKKS_ERANGE, "batch / n_limbs above 65535");
+  return check_device(c);
+}
+
+ckks_status ckks_ntt_fwd(const ckks_ctx* c, uint32_t* data, uint32_t first_prime, uint32_t n_limbs, uint32_t batch,
+                         void* stream) {
+  ckks_status st = ntt_common(c, data, first_prime, n_limbs, batch);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t N = c->h.n;
+  ckks::ColArgs ca{data, (uint64_t)n_limbs * N, first_prime, n_limbs};
+  hipError_t e = ckks::launch_col(c->d, ca, true, false, batch, s);
+  if (e != hipSuccess) return hip_status(e, "column pass");
+  ckks::RowArgs r{};
+  r.src = data;
+  r.dst = data;
+  r.src_item_stride = r.dst_item_stride = (uint64_t)n_limbs * N;
+  r.prime0 = first_prime;
+  r.n_limbs = n_limbs;
+  return hip_status(ckks::launch_row(c->d, r, true, batch, s), "row pass");
+}
+
+ckks_status ckks_ntt_inv(const ckks_ctx* c, uint32_t* data, uint32_t first_prime, uint32_t n_limbs, uint32_t batch,
+                         void* stream) {
+  ckks_status st = ntt_common(c, data, first_prime, n_limbs, batch);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t N = c->h.n;
+  ckks::RowArgs r{};
+  r.src = data;
+  r.dst = data;
+  r.src_item_stride = r.dst_item_stride = (uint64_t)n_limbs * N;
+  r.prime0 = first_prime;
+  r.n_limbs = n_limbs;
+  hipError_t e = ckks::launch_row(c->d, r, false, batch, s);
+  if (e != hipSuccess) return hip_status(e, "row pass");
+  ckks::ColArgs ca{data, (uint64_t)n_limbs * N, first_prime, n_limbs};
+  return hip_status(ckks::launch_col(c->d, ca, false, true, batch, s), "column pass");
+}
+
+ckks_status ckks_modup(const ckks_ctx* cc, const uint32_t* c1, uint32_t level, uint32_t* digits, uint32_t batch,
+                       void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!c1 || !digits) return fail(CKKS_EINVAL, "c1 or digits is NULL");
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Host& h = c->h;
+  const uint64_t N = h.n, El = level + h.K;
+  hipError_t e = run_modup(c, c1, (uint64_t)level * N, level, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  const uint32_t d = digits_at(h, level);
+  for (uint32_t j = 0; j < d; ++j) {
+    ckks::RowArgs r{};
+    r.src = c->ext + (uint64_t)j * (h.L + h.K) * N;
+    r.src_item_stride = (uint64_t)h.dnum * (h.L + h.K) * N;
+    r.dst = digits + (uint64_t)j * El * N;
+    r.dst_item_stride = (uint64_t)d * El * N;
+    r.prime0 = 0;
+    r.n_limbs = (uint32_t)El;
+    r.own_lo = j * h.alpha;
+    r.own_n = std::min(h.alpha, level - j * h.alpha);
+    r.own_src = c1;
+    r.own_item_stride = (uint64_t)level * N;
+    r.level = level;
+    e = ckks::launch_row(c->d, r, true, batch, s);
+    if (e != hipSuccess) return hip_status(e, "ModUp row pass");
+  }
+  return ok();
+}
+
+ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, uint32_t* out, uint32_t batch,
+                         void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!x || !out) return fail(CKKS_EINVAL, "x or out is NULL");
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Host& h = c->h;
+  const uint64_t N = h.n, El = level + h.K;
+  ckks::RowArgs r{};
+  r.src = x + (uint64_t)level * N;
+  r.src_item_stride = El * N;
+  r.dst = c->rowtmp;
+  r.dst_item_stride = (uint64_t)h.K * N;
+  r.prime0 = h.L;
+  r.n_limbs = h.K;
+  hipError_t e = ckks::launch_row(c->d, r, false, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModDown row pass");
+  ckks::ConvArgs a{};
+  a.src = c->rowtmp;
+  a.src_item = (uint64_t)h.K * N;
+  a.src_y = 0;
+  a.dst = c->conv;
+  a.dst_item = (uint64_t)level * N;
+  a.dst_y = 0;
+  a.src_prime0 = h.L;
+  a.src_prime_step = 0;
+  a.ns_max = h.K;
+  a.ns_limit = h.K;
+  a.scale = c->d.md_scale_pl;
+  a.scale_y = 0;
+  a.conv = c->d.md_conv64;
+  a.conv_y = 0;
+  a.conv_s = h.L;
+  a.conv_by_abs = 0;
+  a.n_targets = level;
+  a.skip = 0;
+  a.level = level;
+  e = ckks::launch_conv(c->d, a, 1, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModDown conversion");
+  ckks::RowArgs r2{};
+  r2.src = c->conv;
+  r2.dst = c->conv;
+  r2.src_item_stride = r2.dst_item_stride = (uint64_t)level * N;
+  r2.prime0 = 0;
+  r2.n_limbs = level;
+  e = ckks::launch_row(c->d, r2, true, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModDown row NTT");
+  return hip_status(ckks::launch_moddown_final(c->d, x, El * N, c->conv, (uint64_t)level * N, out,
+                                               (uint64_t)level * N, level, batch, s),
+                    "ModDown final");
+}
+
+ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
+                           const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt, uint32_t* out,
+                           uint32_t batch, void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!ct || !key_b || !out) return fail(CKKS_EINVAL, "ct, key_b or out is NULL");
+  if (!key_a && !key_seed) return fail(CKKS_EINVAL, "need key_a or key_seed");
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_galois(c, galois_elt)) ||
+      (st = check_device(c)))
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t N = c->h.n;
+  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 2ull * level * N, level, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  ckks::KeyRef k{};
+  k.b = key_b;
+  k.a = key_a;
+  if (!key_a) seed_words(key_seed, k.seed);
+  k.galois = galois_elt;
+  e = run_ip_moddown(c, ct, 2ull * level * N, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k,
+                     out, s);
+  return hip_status(e, "inner product / ModDown");
+}
+
+ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, uint32_t n_keys,
+                                   const uint32_t* const* key_b, const uint8_t* key_seeds,
+                                   const uint32_t* const* key_a, const uint32_t* galois_elts, uint32_t* out,
+                                   void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!ct || !key_b || !galois_elts || !out) return fail(CKKS_EINVAL, "ct, key_b, galois_elts or out is NULL");
+  if ((st = check_level(c, level))) return st;
+  if (n_keys < 1 || n_keys > ckks::kMaxHoist) return fail(CKKS_ERANGE, "n_keys %u outside 1..%u", n_keys, ckks::kMaxHoist);
+  for (uint32_t k = 0; k < n_keys; ++k) {
+    if (!key_b[k]) return fail(CKKS_EINVAL, "key_b[%u] is NULL", k);
+    if ((!key_a || !key_a[k]) && !key_seeds) return fail(CKKS_EINVAL, "key %u has neither key_a nor a seed", k);
+    if ((st = check_galois(c, galois_elts[k]))) return st;
+  }
+  if ((st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t N = c->h.n;
+  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 0, level, 1, s);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  const uint32_t chunk = std::min<uint32_t>(c->max_batch, 16);
+  for (uint32_t k0 = 0; k0 < n_keys; k0 += chunk) {
+    const uint32_t nk = std::min(chunk, n_keys - k0);
+    ckks::KeyRef keys[16];
+    for (uint32_t k = 0; k < nk; ++k) {
+      keys[k] = ckks::KeyRef{};
+      keys[k].b = key_b[k0 + k];
+      keys[k].a = key_a ? key_a[k0 + k] : nullptr;
+      if (!keys[k].a) seed_words(key_seeds + 32 * (k0 + k), keys[k].seed);
+      keys[k].galois = galois_elts[k0 + k];
+    }
+    e = run_ip_moddown(c, ct, 0, 0, level, 1, nk, keys, out + (uint64_t)k0 * 2 * level * N, s);
+    if (e != hipSuccess) return hip_status(e, "inner product / ModDown");
+  }
+  return ok();
+}
+
+ckks_status ckks_expand_a(const ckks_ctx* c, const uint8_t* key_seed, uint32_t* key_a, void* stream) {
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!key_seed || !key_a) return fail(CKKS_EINVAL, "key_seed or key_a is NULL");
+  if ((st = check_device(c))) return st;
+  uint32_t w[8];
+  seed_words(key_seed, w);
+  return hip_status(ckks::launch_expand(c->d, w, key_a, c->regen_blocks, (hipStream_t)stream), "expand");
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Internal interface between the host orchestration (api.cpp) and the gfx950
+// kernels (kernels.hip).  Nothing here crosses the C-ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckks {
+
+constexpr uint32_t kRow = 1024;         // row-pass block = ChaCha tile = 2^10 coefficients
+constexpr uint32_t kMaxHoist = 64;      // keys per hoisted call
+constexpr uint32_t kMaxDnum = 8;
+constexpr uint32_t kDefaultRegenBlocks = 68;
+constexpr uint32_t kMaxRegenBlocks = 256;
+
+// Device-resident constant tables of one context.  Pairs (wm, wmq) are a
+// constant w in Montgomery form wm = w*2^32 mod q and its companion wm*q^-1 mod 2^32.
+struct DevTables {
+  uint32_t log_n, n, L, K, dnum, alpha;
+  const uint32_t* q;        // [L+K]
+  const uint32_t* qinv;     // [L+K] q^-1 mod 2^32
+  const uint2* tw;          // [L+K][N]  psi^brv(k)
+  const uint2* itw;         // [L+K][N]  psi^-brv(k)
+  const uint2* ninv;        // [L+K]     N^-1
+  const uint2* mu_scale;    // [L+1][L]  N^-1 * (Qd/q_i)^-1 mod q_i for i's digit at level l
+  const uint32_t* mu_conv;  // [L+1][dnum][alpha][L+K]  (Qd/q_i) * 2^64 mod q_t (plain)
+  const uint2* md_scale_ks; // [K] N^-1 * (P/p_k)^-1 * 2^64 mod p_k
+  const uint2* md_scale_pl; // [K] N^-1 * (P/p_k)^-1 mod p_k
+  const uint32_t* md_conv;  // [K][L] (P/p_k) mod q_i (plain)
+  const uint32_t* md_conv64;// [K][L] (P/p_k) * 2^64 mod q_i (plain)
+  const uint2* md_fin_ks;   // [L] 2^64 * P^-1 mod q_i
+  const uint2* md_fin_pl;   // [L] P^-1 mod q_i
+  const uint32_t* bound;    // [L+K] floor(2^32/q)*q
+  const uint2* one;         // [L+K] 1 (i.e. 2^32 mod q) for w mod q
+};
+
+// Row pass over limbs: blocks of 1024 coefficients, one wave per block.
+struct RowArgs {
+  const uint32_t* src;
+  uint32_t* dst;
+  uint64_t src_item_stride, dst_item_stride;   // words between items
+  uint32_t prime0;           // absolute prime of limb 0
+  uint32_t n_limbs;
+  // ModUp finish mode: limbs [own_lo, own_lo+own_n) are copied from `own_src` untransformed
+  // and the transformed limbs come from src limb index y (y < own_lo) or y - own_n.
+  uint32_t own_lo, own_n;
+  const uint32_t* own_src;
+  uint64_t own_item_stride;
+  // ext-basis prime mapping (limb y -> absolute prime): y < level ? prime0 + y : L + (y - level)
+  uint32_t level;            // 0: plain mapping prime0 + y
+};
+
+// Column pass over limbs (in place): one thread per column of 2^(log_n-10) coefficients.
+struct ColArgs {
+  uint32_t* data;
+  uint64_t item_stride;
+  uint32_t prime0, n_limbs;
+};
+
+// Fused column INTT + scale + fast base conversion + column NTT.
+struct ConvArgs {
+  const uint32_t* src;       // source limbs: src + item*src_item + y*src_y + s*N
+  uint64_t src_item, src_y;
+  uint32_t* dst;             // dst + item*dst_item + y*dst_y + dlimb*N
+  uint64_t dst_item, dst_y;
+  uint32_t src_prime0, src_prime_step;   // absolute prime of source limb s of group y: prime0 + y*step + s
+  uint32_t ns_max, ns_limit;             // ns = min(ns_max, ns_limit - y*src_prime_step)
+  const uint2* scale;        // + y*scale_y + s
+  uint32_t scale_y;
+  const uint32_t* conv;      // + y*conv_y + s*conv_s + abs target prime (or target limb)
+  uint32_t conv_y, conv_s;
+  uint32_t conv_by_abs;      // 1: index conv by absolute target prime, 0: by target limb
+  uint32_t n_targets;        // targets e; dst limb = e < skip_lo ? e : e + ns; abs prime via level map
+  uint32_t skip;             // 1: skip the source limbs' own range in the destination limbs
+  uint32_t level;            // ext mapping: dlimb < level ? dlimb : L + dlimb - level (level=0: dlimb)
+};
+
+struct KeyRef {
+  const uint32_t* b;         // [dnum][L+K][N]
+  const uint32_t* a;         // stored a-half or nullptr
+  uint32_t seed[8];
+  uint32_t galois;
+};
+
+// Inner product (+ fused ModDown pieces).  Grid: x = limb, y = 1024-block, z = key group.
+struct IpArgs {
+  uint32_t level, nd;        // level and its digit count
+  uint32_t n_ct;             // ciphertexts per key group
+  const uint32_t* ext;       // [ext item][dnum][L+K][N]
+  uint64_t ext_ct_stride;    // words between ciphertexts (0 when hoisted: one shared ModUp)
+  const uint32_t* ct;        // [ct][2][level][N]
+  uint64_t ct_ct_stride;     // 0 when hoisted
+  uint32_t* tmpP;            // special output [item][2][K][N]
+  const uint32_t* conv;      // final input   [item][2][level][N] (row pass pending)
+  uint32_t* out;             // final output  [item][2][level][N]
+  uint32_t regen_blocks;
+  uint32_t n_keys;
+  KeyRef key[16];            // per key group (grid z)
+};
+
+hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t items, hipStream_t s);
+hipError_t launch_col(const DevTables& T, const ColArgs& a, bool fwd, bool scale_ninv, uint32_t items, hipStream_t s);
+hipError_t launch_conv(const DevTables& T, const ConvArgs& a, uint32_t groups, uint32_t items, hipStream_t s);
+hipError_t launch_ip(const DevTables& T, const IpArgs& a, bool final_pass, uint32_t n_limbs, hipStream_t s);
+hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
+                         hipStream_t s);
+hipError_t launch_moddown_final(const DevTables& T, const uint32_t* x, uint64_t x_item, const uint32_t* conv,
+                                uint64_t conv_item, uint32_t* out, uint64_t out_item, uint32_t level,
+                                uint32_t items, hipStream_t s);
+
+}  // namespace ckks

@@ -1,0 +1,85 @@
+// 32-bit modular arithmetic for odd primes q < 2^32 (gfx950 device code).
+//
+// Residues are canonical, in [0, q), at every kernel boundary.  The primes of a
+// 2^16-point chain all exceed 2^31, so a + b can carry out of 32 bits and the
+// lazy [0, 2q) forms do not fit a word: every add and subtract here reduces
+// fully.  Multiplication by a constant w uses Montgomery's REDC with R = 2^32
+// on a precomputed pair (w~ = w*R mod q, w~ * q^-1 mod R); a sum of up to ~2^31
+// 64-bit products is kept exactly in three words and brought back to [0, q) by
+// two word-steps of REDC (result carries a factor R^-2 that callers fold into a
+// later constant).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckks {
+
+__host__ __device__ __forceinline__ uint32_t umulhi32(uint32_t a, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __umulhi(a, b);
+#else
+  return (uint32_t)(((uint64_t)a * b) >> 32);
+#endif
+}
+
+struct Mod {
+  uint32_t q;     // the prime
+  uint32_t qinv;  // q^-1 mod 2^32
+};
+
+// a - b mod q for a, b in [0, q)
+__host__ __device__ __forceinline__ uint32_t sub_mod(uint32_t a, uint32_t b, uint32_t q) {
+  uint32_t r = a - b;
+  return (a < b) ? r + q : r;
+}
+
+// a + b mod q for a, b in [0, q): a - (q - b)
+__host__ __device__ __forceinline__ uint32_t add_mod(uint32_t a, uint32_t b, uint32_t q) {
+  return sub_mod(a, q - b, q);
+}
+
+// a * w mod q, where (wm, wmq) = (w*2^32 mod q, wm*qinv mod 2^32); any a < 2^32.
+// REDC(a*wm) with the borrow form: (a*wm - m*q)/2^32 = hi(a*wm) - hi(m*q), m = lo(a*wm)*qinv.
+__host__ __device__ __forceinline__ uint32_t mul_const(uint32_t a, uint32_t wm, uint32_t wmq, uint32_t q) {
+  uint32_t hi = umulhi32(a, wm);
+  uint32_t m = a * wmq;
+  uint32_t t = umulhi32(m, q);
+  return sub_mod(hi, t, q);
+}
+
+// Companion of a Montgomery-form constant: wm * q^-1 mod 2^32.
+__host__ __device__ __forceinline__ uint32_t companion(uint32_t wm, uint32_t qinv) { return wm * qinv; }
+
+// Exact three-word accumulator of 64-bit products.
+struct Acc96 {
+  uint64_t lo;  // low 64 bits
+  uint32_t hi;  // carries out of the low 64 bits
+};
+
+__host__ __device__ __forceinline__ void acc_zero(Acc96& a) {
+  a.lo = 0;
+  a.hi = 0;
+}
+
+__host__ __device__ __forceinline__ void acc_mac(Acc96& a, uint32_t x, uint32_t y) {
+  uint64_t p = (uint64_t)x * (uint64_t)y;
+  uint64_t s = a.lo + p;
+  a.hi += (s < p) ? 1u : 0u;
+  a.lo = s;
+}
+
+// S * 2^-64 mod q for the accumulated S = hi*2^64 + lo, valid while hi + 2 < q.
+// Two word-steps of REDC in the subtract form: with m = w*q^-1 mod 2^32 for the
+// low word w, S - m*q has a zero low word, so (S - m*q)/2^32 = (S >> 32) - hi(m*q).
+// After the first step the value lies in (-q, (hi+1)*2^32); after the second in
+// [-q, hi+1], so one conditional add of q makes it canonical.
+__host__ __device__ __forceinline__ uint32_t acc_redc2(const Acc96& a, Mod md) {
+  const uint32_t a1 = umulhi32((uint32_t)a.lo * md.qinv, md.q);
+  const uint64_t s1 = (((uint64_t)a.hi << 32) | (a.lo >> 32)) - a1;  // two's complement if negative
+  const int32_t h1 = (int32_t)(uint32_t)(s1 >> 32);
+  const uint32_t a2 = umulhi32((uint32_t)s1 * md.qinv, md.q);
+  const int64_t r = (int64_t)h1 - (int64_t)a2;
+  return (uint32_t)(r < 0 ? r + md.q : r);
+}
+
+}  // namespace ckks

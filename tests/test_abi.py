@@ -1,0 +1,107 @@
+"""The C-ABI library without a GPU: it loads, exports what include/ckks_ks.h declares,
+derives the same chain and roots as the oracle, and rejects bad arguments before any launch."""
+import ctypes
+
+import pytest
+
+from oracle.chain import chain_primes as oracle_chain, min_root
+from rns_ckks_key_amd import _lib
+from rns_ckks_key_amd._lib import PCTX, U32, lib
+from rns_ckks_key_amd.api import CkksError, Context, chain_primes
+
+EINVAL, ERANGE, EUNSUPPORTED = -1, -2, -5
+
+
+def test_every_declared_symbol_is_exported():
+    names = _lib.header_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("log_n,bits,count", [(12, 30, 6), (16, 32, 48), (15, 32, 20)])
+def test_chain_matches_oracle(log_n, bits, count):
+    assert chain_primes(log_n, bits, count) == oracle_chain(1 << log_n, bits, count)
+
+
+@pytest.mark.parametrize("log_n,L,K,dnum,bits", [(12, 4, 2, 2, 30), (16, 36, 12, 3, 32)])
+def test_host_context_roots_match_oracle(log_n, L, K, dnum, bits):
+    ctx = Context.for_chain(log_n, L, K, dnum, bits, max_batch=0)
+    assert ctx.n == 1 << log_n and ctx.alpha == -(-L // dnum) and ctx.workspace_bytes == 0
+    qs = oracle_chain(1 << log_n, bits, L + K)
+    assert ctx.primes == qs
+    idx = range(L + K) if log_n == 12 else (0, 17, 35, 36, 47)
+    for t in idx:
+        assert ctx.roots[t] == min_root(qs[t], 1 << log_n)
+    ctx.close()
+
+
+def _create(log_n, num_q, num_p, dnum, primes, max_batch=0):
+    h = PCTX()
+    arr = (U32 * len(primes))(*primes) if primes is not None else None
+    st = lib.ckks_ctx_create(ctypes.byref(h), log_n, num_q, num_p, dnum, arr, max_batch)
+    if st == 0:
+        lib.ckks_ctx_destroy(h)
+    return st
+
+
+def test_ctx_create_rejects_bad_parameters():
+    qs = oracle_chain(1 << 12, 30, 6)
+    assert _create(12, 4, 2, 2, qs) == 0
+    assert _create(12, 4, 2, 2, None) == EINVAL
+    assert _create(11, 4, 2, 2, oracle_chain(1 << 11, 30, 6)) == EUNSUPPORTED
+    assert _create(17, 4, 2, 2, qs) == EUNSUPPORTED
+    bad = list(qs)
+    bad[2] = 8193  # = 1 mod 2N but 3 * 2731
+    assert _create(12, 4, 2, 2, bad) == ERANGE
+    bad = list(qs)
+    bad[1] = qs[1] + 2  # not = 1 mod 2N
+    assert _create(12, 4, 2, 2, bad) == ERANGE
+    bad = list(qs)
+    bad[5] = qs[0]  # repeated prime
+    assert _create(12, 4, 2, 2, bad) == ERANGE
+    assert _create(12, 4, 1, 2, qs[:5]) == ERANGE  # special modulus narrower than a digit
+    assert _create(12, 4, 2, 0, qs) == ERANGE
+    msg = lib.ckks_last_error().decode()
+    assert "dnum" in msg
+
+
+def test_host_context_validates_calls_before_any_launch():
+    ctx = Context.for_chain(12, 4, 2, 2, 30, max_batch=0)
+    h = ctx.handle
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call stops before launching
+    seed = bytes(32)
+
+    def ks(ct=fake, level=4, kb=fake, sd=seed, ka=None, g=5, out=fake, batch=1):
+        return lib.ckks_keyswitch(h, ct, level, kb, sd, ka, g, out, batch, None)
+
+    assert ks(level=0) == ERANGE
+    assert ks(level=5) == ERANGE
+    assert ks(g=4) == ERANGE
+    assert ks(g=2 * 4096 + 1) == ERANGE
+    assert ks(batch=0) == ERANGE
+    assert ks(ct=None) == EINVAL
+    assert ks(kb=None) == EINVAL
+    assert ks(out=None) == EINVAL
+    assert ks(sd=None, ka=None) == EINVAL
+    assert ks() == EINVAL and "host-only" in lib.ckks_last_error().decode()
+    assert lib.ckks_ntt_fwd(h, fake, 5, 2, 1, None) == ERANGE  # limbs 5..6 beyond 6 primes
+    assert lib.ckks_ntt_fwd(h, None, 0, 2, 1, None) == EINVAL
+    assert lib.ckks_ntt_inv(h, fake, 0, 0, 1, None) == ERANGE
+    assert lib.ckks_modup(h, fake, 5, fake, 1, None) == ERANGE
+    assert lib.ckks_moddown(h, fake, 0, fake, 1, None) == ERANGE
+    assert lib.ckks_modup(h, None, 4, fake, 1, None) == EINVAL
+    kb = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    gal = (U32 * 2)(5, 6)
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, fake, None) == ERANGE
+    gal = (U32 * 2)(5, 25)
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 0, kb, seed * 2, None, gal, fake, None) == ERANGE
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, None, None, gal, fake, None) == EINVAL
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, fake, None) == EINVAL
+    assert lib.ckks_expand_a(h, None, fake, None) == EINVAL
+    assert lib.ckks_ctx_set_regen_blocks(h, 63) == ERANGE
+    assert lib.ckks_ctx_set_regen_blocks(h, 64) == 0
+    with pytest.raises(CkksError) as ei:
+        _lib.check(ks(level=9))
+    assert ei.value.name == "CKKS_ERANGE"
+    ctx.close()
