@@ -1,0 +1,263 @@
+"""Benchmark: key-switches/s at N=2^16, 36+12 x 32-bit primes, on one MI355X.
+
+One step = one ckks_keyswitch call on a batch of 8 ciphertexts at level 36 with
+one rotation key (Galois element 5), i.e. the whole hot path (INTT, ModUp,
+inner product with the a-half regenerated in-kernel by ChaCha12, ModDown).
+Inputs are synthetic and seeded (rns_ckks_key_amd.synth, workload 2), resident
+in HBM before timing; R copies of the ciphertexts and keys are rotated so that
+repeated steps cannot be served from the 256 MB Infinity Cache.
+
+Output: one JSON line (rank 0).  Besides the headline (regenerated a-half) it
+carries the stored-key variant, limb-NTTs/s, the roofline of the dominant
+kernel (algorithmic work per launch over its event-timed duration) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+LOG_N, L, K, DNUM, BITS = 16, 36, 12, 3, 32
+N = 1 << LOG_N
+BATCH, LEVEL, GALOIS = 8, 36, 5
+ROTATE = 4
+
+# ---------------------------------------------------------------- work model
+# Algorithmic work in 32-bit VALU lane-op slots (one full-rate op on one lane),
+# with gfx950's measured full-rate 32-bit multiplies: a butterfly is one
+# Montgomery constant multiply (3 multiplies + 3 adds) plus a modular add and a
+# modular subtract; a MAC is a 32x32->64 product accumulated into 96 bits; a
+# reduction is the two-word REDC; ChaCha12 is 12 rounds x 4 quarter rounds x 12
+# ops / 16 words + feed-forward and rejection.
+SLOT = {"bfly": 13, "cmul": 6, "mac": 5, "red": 9, "chacha_word": 42}
+VALU_PEAK = 256 * 4 * 16 * 2.4e9      # lane-op slots/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+HBM_PEAK = 8.0e12                      # bytes/s
+
+
+def digits(level: int, alpha: int) -> list[int]:
+    return [min(alpha, level - j * alpha) for j in range((level + alpha - 1) // alpha)]
+
+
+def work_model(level: int, batch: int, regen: bool, n_keys: int = 1) -> dict:
+    """Slots per launch of each kernel class of one key-switch call (batch ct, one key each group)."""
+    alpha = -(-L // DNUM)
+    dg = digits(level, alpha)
+    d = len(dg)
+    logc = LOG_N - 10
+    col = N // 2 * logc           # butterflies of one column pass over a limb
+    row = N // 2 * 10             # butterflies of one row pass over a limb
+    e = level + K
+    items = batch * n_keys
+    w = {}
+    w["row"] = batch * level * row * SLOT["bfly"]
+    mu = 0
+    for a in dg:
+        mu += a * col * SLOT["bfly"] + a * N * SLOT["cmul"]
+        mu += (e - a) * N * (a * SLOT["mac"] + SLOT["red"]) + (e - a) * col * SLOT["bfly"]
+    w["modup_conv"] = batch * mu
+    rej = 0.0075  # mean rejection rate over the chain's 48 primes
+    words_special = d * K * N * (1 + rej) if regen else 0
+    words_final = d * level * N * (1 + rej) if regen else 0
+    w["ip_special"] = items * K * (d * row * SLOT["bfly"] + 2 * d * N * SLOT["mac"] + 2 * N * SLOT["red"]
+                                   + 2 * row * SLOT["bfly"]) + n_keys * words_special * SLOT["chacha_word"]
+    w["moddown_conv"] = items * 2 * (K * col * SLOT["bfly"] + K * N * SLOT["cmul"]
+                                     + level * N * (K * SLOT["mac"] + SLOT["red"]) + level * col * SLOT["bfly"])
+    w["ip_final"] = items * level * ((d - 1) * row * SLOT["bfly"] + 2 * row * SLOT["bfly"] + 2 * d * N * SLOT["mac"]
+                                     + 2 * N * SLOT["red"] + 2 * N * SLOT["cmul"] + 4 * N) \
+        + n_keys * words_final * SLOT["chacha_word"]
+    return w
+
+
+def hbm_bytes(level: int, batch: int, regen: bool, n_keys: int = 1) -> float:
+    """Compulsory bytes of one call: ciphertexts in and out, and the key rows it must read once."""
+    d = len(digits(level, -(-L // DNUM)))
+    ct = batch * 2 * level * N * 4
+    out = batch * n_keys * 2 * level * N * 4
+    key_rows = d * (level + K) * N * 4
+    return ct + out + n_keys * key_rows * (1 if regen else 2)
+
+
+# ---------------------------------------------------------------- helpers
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "modarith.h", "ckks_internal.h"):
+        with open(os.path.join(ROOT, "rns_ckks_key_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str) -> dict | None:
+    """Per-launch HBM bytes of `kernel` from the committed rocprofv3 counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_keyswitch_batch8_l36.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel-source-hash:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^\|\s*{kernel}\s*\|\s*([0-9.e+]+)\s*\|\s*([0-9.e+]+)\s*\|", text, re.M)
+    if not m:
+        return None
+    return {"fetch_bytes": float(m.group(1)), "write_bytes": float(m.group(2))}
+
+
+def time_calls(fn, steps: int, warmup: int, torch) -> float:
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(steps):
+        fn(i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def cpu_baseline(primes, draw, budget_s: float) -> dict:
+    """The oracle as it stands, on host cores, on ciphertexts of the same workload."""
+    import numpy as np
+
+    from oracle import ks as oks
+    from oracle.params import Params
+
+    pr = Params.make(LOG_N, L, K, DNUM, BITS)
+    assert pr.primes == list(primes), "library and oracle chains differ"
+    key_b = np.asarray(draw["key_b"], dtype=np.uint64)
+    done, t0 = 0, time.perf_counter()
+    for b in range(BATCH):
+        ct = draw["cts"][b].astype(np.uint64)
+        oks.keyswitch(pr, ct, LEVEL, key_b, GALOIS, seed=draw["seed"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "key-switches/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of the 8 ciphertexts at level 36, g=5, a-half regenerated from the seed "
+                      f"(numpy, single-threaded elementwise); {dt:.1f} s on {len(os.sched_getaffinity(0))} "
+                      f"available host cores"}
+
+
+# ---------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: key-switching is not sharded across GPUs in this library "
+              "(see the design notes); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from rns_ckks_key_amd import synth
+    from rns_ckks_key_amd.api import Context, chain_primes, to_device
+
+    torch.cuda.set_device(0)
+    primes = chain_primes(LOG_N, BITS, L + K)
+    ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+    d = synth.draw(2, primes)
+    seed = d.keys[0].seed
+    cts = np.stack(d.cts)                                   # [8][2][36][N]
+    kb_host = synth.uniform_key_rows(2000 + 2, primes, DNUM, N)
+    dev_ct = [to_device(cts)]
+    dev_kb = [to_device(kb_host)]
+    for r in range(1, ROTATE):  # distinct copies: the next step's inputs are not in the Infinity Cache
+        dev_ct.append(dev_ct[0].clone())
+        dev_kb.append(dev_kb[0].clone())
+    dev_ka = [ctx.expand_a(seed) for _ in range(ROTATE)]
+    outs = [torch.empty((BATCH, 2, LEVEL, N), dtype=torch.int32, device="cuda") for _ in range(ROTATE)]
+    torch.cuda.synchronize()
+
+    def step(i, regen):
+        r = i % ROTATE
+        ctx.keyswitch(dev_ct[r], LEVEL, dev_kb[r], GALOIS, key_seed=seed if regen else None,
+                      key_a=None if regen else dev_ka[r], out=outs[r])
+
+    res = {}
+    for variant, regen in (("regen", True), ("stored", False)):
+        ms = time_calls(lambda i: step(i, regen), args.steps, args.warmup, torch)
+        ctx.profile(True)
+        for i in range(args.steps):
+            step(i, regen)
+        ctx.profile(False)
+        prof = ctx.profile_read()
+        res[variant] = {"ms_per_step": ms, "key_switches_per_s": BATCH / (ms * 1e-3), "prof": prof}
+        print(f"[bench] {variant}: {ms:.3f} ms per batch of {BATCH}", file=sys.stderr, flush=True)
+
+    # limb-NTTs/s on [8][72][N]
+    x = torch.randint(0, 2**31 - 1, (BATCH, 2 * LEVEL, N), dtype=torch.int32, device="cuda")
+    xr = x.view(BATCH * 2, LEVEL, N)
+    ms_f = time_calls(lambda i: ctx.ntt_fwd(xr, 0), args.steps, args.warmup, torch)
+    ms_i = time_calls(lambda i: ctx.ntt_inv(xr, 0), args.steps, args.warmup, torch)
+    limbs = BATCH * 2 * LEVEL
+
+    head = res["regen"]
+    wm = work_model(LEVEL, BATCH, True)
+    prof = head["prof"]
+    per_launch = {k: prof[k][0] / prof[k][1] for k in prof if prof[k][1]}
+    dominant = max(per_launch, key=lambda k: prof[k][0])
+    t_dom = per_launch[dominant] * 1e-3
+    achieved = wm[dominant] / t_dom
+    traffic = read_traffic(dominant)
+    total_slots = sum(wm.values())
+    t_call = head["ms_per_step"] * 1e-3
+    out = {
+        "metric": "key-switches/sec at N=2^16, 36+12 x 32-bit primes; % of HBM roofline",
+        "value": round(head["key_switches_per_s"], 1),
+        "unit": "key-switches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "single key-switch at bootstrapping scale: batch 8 ciphertexts, level 36, "
+                               "one rotation key g=5, a-half regenerated in-kernel by ChaCha12",
+                   "N": N, "L": L, "K": K, "dnum": DNUM, "batch": BATCH, "level": LEVEL, "galois": GALOIS,
+                   "variant": "regen", "input_copies_rotated": ROTATE},
+        "roofline": {"bound": "alu", "kernel": dominant, "achieved": round(achieved / 1e12, 3),
+                     "peak": round(VALU_PEAK / 1e12, 3), "unit": "T lane-op slots/s",
+                     "frac": round(achieved / VALU_PEAK, 4),
+                     "work_per_launch_slots": wm[dominant], "avg_launch_ms": round(per_launch[dominant], 4),
+                     "traffic": None if traffic is None else traffic["fetch_bytes"] + traffic["write_bytes"]},
+        "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, True) / t_call / HBM_PEAK, 4),
+        "valu_frac_whole_call": round(total_slots / t_call / VALU_PEAK, 4),
+        "stored_key": {"value": round(res["stored"]["key_switches_per_s"], 1),
+                       "ms_per_step": round(res["stored"]["ms_per_step"], 4),
+                       "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, False) / (res["stored"]["ms_per_step"] * 1e-3)
+                                                  / HBM_PEAK, 4)},
+        "kernel_ms_per_call": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]},
+        "ntt_limbs_per_s": {"forward": round(limbs / (ms_f * 1e-3)), "inverse": round(limbs / (ms_i * 1e-3)),
+                            "shape": [BATCH * 2, LEVEL, N]},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(primes, {"cts": cts, "key_b": kb_host, "seed": seed}, args.cpu_budget)
+    print(json.dumps(out))
+    ctx.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -141,6 +141,30 @@ ckks_status ckks_expand_a(const ckks_ctx *ctx, const uint8_t *key_seed, uint32_t
  * with a rejected word through the continuation path. */
 ckks_status ckks_ctx_set_regen_blocks(ckks_ctx *ctx, uint32_t blocks);
 
+/* Kernel classes of the per-kernel event timer. */
+typedef enum {
+  CKKS_K_ROW = 0,          /* row pass of an NTT/INTT (1024-coefficient blocks) */
+  CKKS_K_COL = 1,          /* column pass of an NTT/INTT */
+  CKKS_K_MODUP_CONV = 2,   /* fused column INTT + ModUp conversion + column NTT */
+  CKKS_K_IP_SPECIAL = 3,   /* inner product over the special primes (+ row INTT) */
+  CKKS_K_MODDOWN_CONV = 4, /* fused column INTT + P->Q conversion + column NTT */
+  CKKS_K_IP_FINAL = 5,     /* inner product over the ciphertext primes + end of ModDown */
+  CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
+  CKKS_K_MODDOWN_FINAL = 7,/* end of the standalone ModDown */
+  CKKS_K_CLASSES = 8
+} ckks_kernel_class;
+
+/* Measurement aid: while enabled, every launch of this context is bracketed by
+ * two HIP events recorded on the call's stream (at most 8192 launches are kept;
+ * later ones are not timed).  Enabling clears earlier records; disabling keeps
+ * them for ckks_profile_read.  Errors: EINVAL (NULL or host-only context). */
+ckks_status ckks_profile_enable(ckks_ctx *ctx, int enable);
+
+/* Waits for the recorded events and writes, for each kernel class c <
+ * n_classes, the summed kernel time in milliseconds (ms_out[c], host) and the
+ * number of timed launches (launches_out[c], host; may be NULL). */
+ckks_status ckks_profile_read(ckks_ctx *ctx, double *ms_out, uint32_t *launches_out, uint32_t n_classes);
+
 #ifdef __cplusplus
 }
 #endif

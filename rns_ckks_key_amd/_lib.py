@@ -51,7 +51,11 @@ _SIGS = {
                                               ctypes.POINTER(P), PU32, P, P]),
     "ckks_expand_a": (ctypes.c_int, [PCTX, ctypes.c_char_p, P, P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
+    "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
+    "ckks_profile_read": (ctypes.c_int, [PCTX, ctypes.POINTER(ctypes.c_double), PU32, U32]),
 }
+
+KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final"]
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import PCTX, U32, U64, CkksError, check, lib
+from ._lib import KERNEL_CLASSES, PCTX, U32, U64, CkksError, check, lib
 
 __all__ = ["Context", "CkksError", "chain_primes", "to_device", "to_numpy"]
 
@@ -102,6 +102,18 @@ class Context:
 
     def set_regen_blocks(self, blocks: int) -> None:
         check(lib.ckks_ctx_set_regen_blocks(self._h, blocks))
+
+    def profile(self, enable: bool) -> None:
+        """Bracket every launch with HIP events on its stream (measurement aid)."""
+        check(lib.ckks_profile_enable(self._h, 1 if enable else 0))
+
+    def profile_read(self) -> dict:
+        """{kernel class: (summed ms, launches)} for the launches timed since profiling was enabled."""
+        n = len(KERNEL_CLASSES)
+        ms = (ctypes.c_double * n)()
+        cnt = (U32 * n)()
+        check(lib.ckks_profile_read(self._h, ms, cnt, n))
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
 
     # ---- transforms
     def ntt_fwd(self, data: torch.Tensor, first_prime: int = 0) -> torch.Tensor:

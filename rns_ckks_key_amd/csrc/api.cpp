@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -226,7 +227,33 @@ struct ckks_ctx {
   uint32_t* ext = nullptr;     // [B][dnum][L+K][N]
   uint32_t* tmpP = nullptr;    // [B][2][K][N]
   uint32_t* conv = nullptr;    // [B][2][L][N]
+  // per-launch event timer (measurement aid)
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_ev;     // pool: 2 events per record
+  std::vector<int> prof_cls;           // class of each record
 };
+
+namespace {
+
+constexpr size_t kProfMax = 8192;
+
+// Brackets one launch with events on `s` when the context's timer is on.
+struct ProfScope {
+  ckks_ctx* c;
+  hipStream_t s;
+  size_t rec;
+  ProfScope(ckks_ctx* ctx, int cls, hipStream_t st) : c(ctx), s(st), rec(SIZE_MAX) {
+    if (!c->prof_on || c->prof_cls.size() >= kProfMax) return;
+    rec = c->prof_cls.size();
+    c->prof_cls.push_back(cls);
+    (void)hipEventRecord(c->prof_ev[2 * rec], s);
+  }
+  ~ProfScope() {
+    if (rec != SIZE_MAX) (void)hipEventRecord(c->prof_ev[2 * rec + 1], s);
+  }
+};
+
+}  // namespace
 
 namespace {
 
@@ -324,7 +351,11 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
   r.n_limbs = level;
   r.own_lo = r.own_n = 0;
   r.level = 0;
-  hipError_t e = ckks::launch_row(c->d, r, false, items, s);
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, false, items, s);
+  }
   if (e != hipSuccess) return e;
   ckks::ConvArgs a{};
   a.src = c->rowtmp;
@@ -346,6 +377,7 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
   a.skip = 1;
   a.level = level;
   a.n_targets = 0;  // per digit: level + K - (digit size), computed in the kernel
+  ProfScope p(c, CKKS_K_MODUP_CONV, s);
   return ckks::launch_conv(c->d, a, digits_at(h, level), items, s);
   return hipSuccess;
 }
@@ -370,7 +402,11 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   ip.regen_blocks = c->regen_blocks;
   ip.n_keys = n_keys;
   for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
-  hipError_t e = ckks::launch_ip(c->d, ip, false, h.K, s);
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_IP_SPECIAL, s);
+    e = ckks::launch_ip(c->d, ip, false, h.K, s);
+  }
   if (e != hipSuccess) return e;
   ckks::ConvArgs a{};
   a.src = c->tmpP;
@@ -392,8 +428,12 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   a.n_targets = level;
   a.skip = 0;
   a.level = level;
-  e = ckks::launch_conv(c->d, a, 2, n_ct * n_keys, s);
+  {
+    ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
+    e = ckks::launch_conv(c->d, a, 2, n_ct * n_keys, s);
+  }
   if (e != hipSuccess) return e;
+  ProfScope p(c, CKKS_K_IP_FINAL, s);
   return ckks::launch_ip(c->d, ip, true, level, s);
 }
 
@@ -489,6 +529,7 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
 
 void ckks_ctx_destroy(ckks_ctx* c) {
   if (!c) return;
+  for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   if (c->ws) (void)hipFree(c->ws);
   if (c->dev_tables) (void)hipFree(c->dev_tables);
   delete c;
@@ -535,7 +576,12 @@ ckks_status ckks_ntt_fwd(const ckks_ctx* c, uint32_t* data, uint32_t first_prime
   hipStream_t s = (hipStream_t)stream;
   const uint64_t N = c->h.n;
   ckks::ColArgs ca{data, (uint64_t)n_limbs * N, first_prime, n_limbs};
-  hipError_t e = ckks::launch_col(c->d, ca, true, false, batch, s);
+  ckks_ctx* cm = const_cast<ckks_ctx*>(c);
+  hipError_t e;
+  {
+    ProfScope p(cm, CKKS_K_COL, s);
+    e = ckks::launch_col(c->d, ca, true, false, batch, s);
+  }
   if (e != hipSuccess) return hip_status(e, "column pass");
   ckks::RowArgs r{};
   r.src = data;
@@ -543,6 +589,7 @@ ckks_status ckks_ntt_fwd(const ckks_ctx* c, uint32_t* data, uint32_t first_prime
   r.src_item_stride = r.dst_item_stride = (uint64_t)n_limbs * N;
   r.prime0 = first_prime;
   r.n_limbs = n_limbs;
+  ProfScope p(cm, CKKS_K_ROW, s);
   return hip_status(ckks::launch_row(c->d, r, true, batch, s), "row pass");
 }
 
@@ -558,9 +605,15 @@ ckks_status ckks_ntt_inv(const ckks_ctx* c, uint32_t* data, uint32_t first_prime
   r.src_item_stride = r.dst_item_stride = (uint64_t)n_limbs * N;
   r.prime0 = first_prime;
   r.n_limbs = n_limbs;
-  hipError_t e = ckks::launch_row(c->d, r, false, batch, s);
+  ckks_ctx* cm = const_cast<ckks_ctx*>(c);
+  hipError_t e;
+  {
+    ProfScope p(cm, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, false, batch, s);
+  }
   if (e != hipSuccess) return hip_status(e, "row pass");
   ckks::ColArgs ca{data, (uint64_t)n_limbs * N, first_prime, n_limbs};
+  ProfScope p(cm, CKKS_K_COL, s);
   return hip_status(ckks::launch_col(c->d, ca, false, true, batch, s), "column pass");
 }
 
@@ -590,7 +643,10 @@ ckks_status ckks_modup(const ckks_ctx* cc, const uint32_t* c1, uint32_t level, u
     r.own_src = c1;
     r.own_item_stride = (uint64_t)level * N;
     r.level = level;
-    e = ckks::launch_row(c->d, r, true, batch, s);
+    {
+      ProfScope p(c, CKKS_K_ROW, s);
+      e = ckks::launch_row(c->d, r, true, batch, s);
+    }
     if (e != hipSuccess) return hip_status(e, "ModUp row pass");
   }
   return ok();
@@ -613,7 +669,11 @@ ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, 
   r.dst_item_stride = (uint64_t)h.K * N;
   r.prime0 = h.L;
   r.n_limbs = h.K;
-  hipError_t e = ckks::launch_row(c->d, r, false, batch, s);
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, false, batch, s);
+  }
   if (e != hipSuccess) return hip_status(e, "ModDown row pass");
   ckks::ConvArgs a{};
   a.src = c->rowtmp;
@@ -635,7 +695,10 @@ ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, 
   a.n_targets = level;
   a.skip = 0;
   a.level = level;
-  e = ckks::launch_conv(c->d, a, 1, batch, s);
+  {
+    ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
+    e = ckks::launch_conv(c->d, a, 1, batch, s);
+  }
   if (e != hipSuccess) return hip_status(e, "ModDown conversion");
   ckks::RowArgs r2{};
   r2.src = c->conv;
@@ -643,8 +706,12 @@ ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, 
   r2.src_item_stride = r2.dst_item_stride = (uint64_t)level * N;
   r2.prime0 = 0;
   r2.n_limbs = level;
-  e = ckks::launch_row(c->d, r2, true, batch, s);
+  {
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r2, true, batch, s);
+  }
   if (e != hipSuccess) return hip_status(e, "ModDown row NTT");
+  ProfScope p(c, CKKS_K_MODDOWN_FINAL, s);
   return hip_status(ckks::launch_moddown_final(c->d, x, El * N, c->conv, (uint64_t)level * N, out,
                                                (uint64_t)level * N, level, batch, s),
                     "ModDown final");
@@ -719,7 +786,45 @@ ckks_status ckks_expand_a(const ckks_ctx* c, const uint8_t* key_seed, uint32_t* 
   if ((st = check_device(c))) return st;
   uint32_t w[8];
   seed_words(key_seed, w);
+  ProfScope p(const_cast<ckks_ctx*>(c), CKKS_K_EXPAND, (hipStream_t)stream);
   return hip_status(ckks::launch_expand(c->d, w, key_a, c->regen_blocks, (hipStream_t)stream), "expand");
+}
+
+ckks_status ckks_profile_enable(ckks_ctx* c, int enable) {
+  ckks_status st = check_ctx(c);
+  if (st || (st = check_device(c))) return st;
+  if (enable) {
+    if (c->prof_ev.empty()) {
+      c->prof_ev.resize(2 * kProfMax);
+      for (auto& e : c->prof_ev)
+        if (hipEventCreate(&e) != hipSuccess) return fail(CKKS_EHIP, "hipEventCreate failed");
+    }
+    c->prof_cls.clear();
+  }
+  c->prof_on = enable != 0;
+  return ok();
+}
+
+ckks_status ckks_profile_read(ckks_ctx* c, double* ms_out, uint32_t* launches_out, uint32_t n_classes) {
+  ckks_status st = check_ctx(c);
+  if (st || (st = check_device(c))) return st;
+  if (!ms_out) return fail(CKKS_EINVAL, "ms_out is NULL");
+  for (uint32_t k = 0; k < n_classes; ++k) {
+    ms_out[k] = 0.0;
+    if (launches_out) launches_out[k] = 0;
+  }
+  for (size_t r = 0; r < c->prof_cls.size(); ++r) {
+    const int k = c->prof_cls[r];
+    if (hipEventSynchronize(c->prof_ev[2 * r + 1]) != hipSuccess) return fail(CKKS_EHIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->prof_ev[2 * r], c->prof_ev[2 * r + 1]) != hipSuccess)
+      return fail(CKKS_EHIP, "hipEventElapsedTime failed");
+    if ((uint32_t)k < n_classes) {
+      ms_out[k] += ms;
+      if (launches_out) launches_out[k] += 1;
+    }
+  }
+  return ok();
 }
 
 }  // extern "C"
