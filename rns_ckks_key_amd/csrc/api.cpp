@@ -112,6 +112,8 @@ uint2 mont(uint32_t w, uint32_t q) {  // (w*2^32 mod q, companion)
   return make_uint2(wm, wm * inv2_32(q));
 }
 
+uint32_t r32(uint32_t q) { return (uint32_t)((1ull << 32) % q); }  // 2^32 mod q
+
 uint32_t r64(uint32_t q) {  // 2^64 mod q
   uint32_t r32 = (uint32_t)((1ull << 32) % q);
   return mulmod(r32, r32, q);
@@ -191,13 +193,13 @@ void build_tables(Host& h) {
       if (k2 != k) ph = mulmod(ph, h.q[L + k2] % pk, pk);
     const uint32_t base = mulmod(invmod(ph, pk), invmod(n % pk, pk), pk);
     h.md_scale_pl[k] = mont(base, pk);
-    h.md_scale_ks[k] = mont(mulmod(base, r64(pk), pk), pk);
+    h.md_scale_ks[k] = mont(mulmod(base, r32(pk), pk), pk);
     for (uint32_t i = 0; i < L; ++i) {
       const uint32_t qi = h.q[i];
       uint32_t v = 1;
       for (uint32_t k2 = 0; k2 < K; ++k2)
         if (k2 != k) v = mulmod(v, h.q[L + k2] % qi, qi);
-      h.md_conv[(size_t)k * L + i] = v;
+      h.md_conv[(size_t)k * L + i] = mulmod(v, r32(qi), qi);
       h.md_conv64[(size_t)k * L + i] = mulmod(v, r64(qi), qi);
     }
   }
@@ -207,7 +209,7 @@ void build_tables(Host& h) {
     for (uint32_t k = 0; k < K; ++k) p = mulmod(p, h.q[L + k] % qi, qi);
     const uint32_t pinv = invmod(p, qi);
     h.md_fin_pl[i] = mont(pinv, qi);
-    h.md_fin_ks[i] = mont(mulmod(pinv, r64(qi), qi), qi);
+    h.md_fin_ks[i] = mont(mulmod(pinv, r32(qi), qi), qi);
   }
 }
 
@@ -468,7 +470,7 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
   if (dnum < 1 || dnum > ckks::kMaxDnum || dnum > num_q) return fail(CKKS_ERANGE, "dnum %u outside 1..min(%u, num_q)", dnum, ckks::kMaxDnum);
   const uint32_t alpha = (num_q + dnum - 1) / dnum;
   if (num_p < alpha) return fail(CKKS_ERANGE, "num_p %u below the digit width %u", num_p, alpha);
-  if (alpha > 24 || num_p > 24) return fail(CKKS_EUNSUPPORTED, "digit width %u / num_p %u above 24", alpha, num_p);
+  if (alpha > 16 || num_p > 16) return fail(CKKS_EUNSUPPORTED, "digit width %u / num_p %u above 16", alpha, num_p);
   const uint32_t n = 1u << log_n;
   for (uint32_t t = 0; t < num_q + num_p; ++t) {
     const uint32_t q = primes[t];

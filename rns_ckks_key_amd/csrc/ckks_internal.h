@@ -23,11 +23,11 @@ struct DevTables {
   const uint2* ninv;        // [L+K]     N^-1
   const uint2* mu_scale;    // [L+1][L]  N^-1 * (Qd/q_i)^-1 mod q_i for i's digit at level l
   const uint32_t* mu_conv;  // [L+1][dnum][alpha][L+K]  (Qd/q_i) * 2^64 mod q_t (plain)
-  const uint2* md_scale_ks; // [K] N^-1 * (P/p_k)^-1 * 2^64 mod p_k
+  const uint2* md_scale_ks; // [K] N^-1 * (P/p_k)^-1 * 2^32 mod p_k (inner-product sums carry 2^-32)
   const uint2* md_scale_pl; // [K] N^-1 * (P/p_k)^-1 mod p_k
-  const uint32_t* md_conv;  // [K][L] (P/p_k) mod q_i (plain)
+  const uint32_t* md_conv;  // [K][L] (P/p_k) * 2^32 mod q_i (plain; REDC2 leaves z * 2^-32)
   const uint32_t* md_conv64;// [K][L] (P/p_k) * 2^64 mod q_i (plain)
-  const uint2* md_fin_ks;   // [L] 2^64 * P^-1 mod q_i
+  const uint2* md_fin_ks;   // [L] 2^32 * P^-1 mod q_i
   const uint2* md_fin_pl;   // [L] P^-1 mod q_i
   const uint32_t* bound;    // [L+K] floor(2^32/q)*q
   const uint2* one;         // [L+K] 1 (i.e. 2^32 mod q) for w mod q

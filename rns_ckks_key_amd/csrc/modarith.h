@@ -47,6 +47,14 @@ __host__ __device__ __forceinline__ uint32_t mul_const(uint32_t a, uint32_t wm, 
   return sub_mod(hi, t, q);
 }
 
+// a * b * 2^-32 mod q for a, b < q (REDC of the full product, subtract form).
+__host__ __device__ __forceinline__ uint32_t mont_mul(uint32_t a, uint32_t b, Mod md) {
+  const uint32_t lo = a * b;
+  const uint32_t hi = umulhi32(a, b);
+  const uint32_t t = umulhi32(lo * md.qinv, md.q);
+  return sub_mod(hi, t, md.q);
+}
+
 // Companion of a Montgomery-form constant: wm * q^-1 mod 2^32.
 __host__ __device__ __forceinline__ uint32_t companion(uint32_t wm, uint32_t qinv) { return wm * qinv; }
 
