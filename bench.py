@@ -159,6 +159,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
+                    help="which key variants to time (the headline is always the regenerated one when timed)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (xor with 0) three times, to calibrate HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: key-switching is not sharded across GPUs in this library "
@@ -167,6 +171,15 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.randint(0, 2**31 - 1, (128 << 20,), dtype=torch.int32, device="cuda")  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_xor(src, 0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 3}))
+        return 0
 
     from rns_ckks_key_amd import synth
     from rns_ckks_key_amd.api import Context, chain_primes, to_device
@@ -193,7 +206,8 @@ def main() -> int:
                       key_a=None if regen else dev_ka[r], out=outs[r])
 
     res = {}
-    for variant, regen in (("regen", True), ("stored", False)):
+    variants = [v for v in (("regen", True), ("stored", False)) if args.variant in ("both", v[0])]
+    for variant, regen in variants:
         ms = time_calls(lambda i: step(i, regen), args.steps, args.warmup, torch)
         ctx.profile(True)
         for i in range(args.steps):
@@ -210,8 +224,9 @@ def main() -> int:
     ms_i = time_calls(lambda i: ctx.ntt_inv(xr, 0), args.steps, args.warmup, torch)
     limbs = BATCH * 2 * LEVEL
 
-    head = res["regen"]
-    wm = work_model(LEVEL, BATCH, True)
+    head_name = "regen" if "regen" in res else "stored"
+    head = res[head_name]
+    wm = work_model(LEVEL, BATCH, head_name == "regen")
     prof = head["prof"]
     per_launch = {k: prof[k][0] / prof[k][1] for k in prof if prof[k][1]}
     dominant = max(per_launch, key=lambda k: prof[k][0])
@@ -242,16 +257,18 @@ def main() -> int:
                      "frac": round(achieved / VALU_PEAK, 4),
                      "work_per_launch_slots": wm[dominant], "avg_launch_ms": round(per_launch[dominant], 4),
                      "traffic": None if traffic is None else traffic["fetch_bytes"] + traffic["write_bytes"]},
-        "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, True) / t_call / HBM_PEAK, 4),
+        "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, head_name == "regen") / t_call / HBM_PEAK, 4),
         "valu_frac_whole_call": round(total_slots / t_call / VALU_PEAK, 4),
-        "stored_key": {"value": round(res["stored"]["key_switches_per_s"], 1),
-                       "ms_per_step": round(res["stored"]["ms_per_step"], 4),
-                       "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, False) / (res["stored"]["ms_per_step"] * 1e-3)
-                                                  / HBM_PEAK, 4)},
         "kernel_ms_per_call": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]},
         "ntt_limbs_per_s": {"forward": round(limbs / (ms_f * 1e-3)), "inverse": round(limbs / (ms_i * 1e-3)),
                             "shape": [BATCH * 2, LEVEL, N]},
     }
+    out["config"]["variant"] = head_name
+    if "stored" in res and head_name != "stored":
+        st = res["stored"]
+        out["stored_key"] = {"value": round(st["key_switches_per_s"], 1), "ms_per_step": round(st["ms_per_step"], 4),
+                             "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, False) / (st["ms_per_step"] * 1e-3)
+                                                        / HBM_PEAK, 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(primes, {"cts": cts, "key_b": kb_host, "seed": seed}, args.cpu_budget)
     print(json.dumps(out))
