@@ -27,15 +27,18 @@ struct Mod {
   uint32_t qinv;  // q^-1 mod 2^32
 };
 
-// a - b mod q for a, b in [0, q)
+// a - b mod q for a, b in [0, q): the borrow of the 32-bit subtraction selects a - b + q.
 __host__ __device__ __forceinline__ uint32_t sub_mod(uint32_t a, uint32_t b, uint32_t q) {
-  uint32_t r = a - b;
-  return (a < b) ? r + q : r;
+  uint32_t d;
+  const bool borrow = __builtin_sub_overflow(a, b, &d);
+  return borrow ? d + q : d;
 }
 
-// a + b mod q for a, b in [0, q): a - (q - b)
+// a + b mod q for a, b in [0, q): a + b when a < q - b, else a - (q - b) (no 33-bit sum needed).
 __host__ __device__ __forceinline__ uint32_t add_mod(uint32_t a, uint32_t b, uint32_t q) {
-  return sub_mod(a, q - b, q);
+  uint32_t d;
+  const bool borrow = __builtin_sub_overflow(a, q - b, &d);
+  return borrow ? a + b : d;
 }
 
 // a * w mod q, where (wm, wmq) = (w*2^32 mod q, wm*qinv mod 2^32); any a < 2^32.
