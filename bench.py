@@ -159,6 +159,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5], default=2,
+                    help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
+                         "5: mixed 64-ciphertext stream")
     ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
                     help="which key variants to time (the headline is always the regenerated one when timed)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +188,8 @@ def main() -> int:
     from rns_ckks_key_amd.api import Context, chain_primes, to_device
 
     torch.cuda.set_device(0)
+    if args.workload != 2:
+        return other_workload(args)
     primes = chain_primes(LOG_N, BITS, L + K)
     ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
     d = synth.draw(2, primes)
@@ -272,6 +277,85 @@ def main() -> int:
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(primes, {"cts": cts, "key_b": kb_host, "seed": seed}, args.cpu_budget)
     print(json.dumps(out))
+    ctx.close()
+    return 0
+
+
+def other_workload(args) -> int:
+    """Workloads 3-5: one JSON line each (not the headline); kernel times from the event timer."""
+    import numpy as np
+    import torch
+
+    from rns_ckks_key_amd import synth
+    from rns_ckks_key_amd.api import Context, chain_primes, to_device
+
+    primes = chain_primes(LOG_N, BITS, L + K)
+    wl = synth.WORKLOADS[args.workload]
+    d = synth.draw(args.workload, primes)
+    variants = [v for v in ("regen", "stored") if args.variant in ("both", v)]
+    res = {"metric": f"workload {args.workload}: {wl.name}", "unit": "key-switches/s", "n_gpus": 1,
+           "dtype": "u32", "data": "synthetic", "steps": args.steps, "warmup": args.warmup}
+    if args.workload == 3:
+        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
+        kb = to_device(synth.uniform_key_rows(3003, primes, DNUM, N))
+        seed = d.keys[0].seed
+        ka = ctx.expand_a(seed)
+        per = {}
+        for li, level in enumerate(wl.levels):
+            cts = to_device(np.stack(d.cts[16 * li:16 * li + 16]))
+            out = torch.empty((16, 2, level, N), dtype=torch.int32, device="cuda")
+            for v in variants:
+                fn = (lambda i, lv=level, c=cts, o=out, v=v: ctx.keyswitch(c, lv, kb, 5, key_seed=seed if v == "regen"
+                                                                           else None, key_a=ka if v == "stored"
+                                                                           else None, out=o))
+                ms = time_calls(fn, args.steps, args.warmup, torch)
+                ctx.profile(True)
+                for i in range(args.steps):
+                    fn(i)
+                ctx.profile(False)
+                prof = ctx.profile_read()
+                per[f"l{level}_{v}"] = {"key_switches_per_s": round(16 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                                        "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+        res["levels"] = per
+    elif args.workload == 4:
+        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
+        ct = to_device(d.cts[0])
+        kbs = [to_device(synth.uniform_key_rows(4000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
+        kas = [ctx.expand_a(kd.seed) for kd in d.keys]
+        out = torch.empty((16, 2, LEVEL, N), dtype=torch.int32, device="cuda")
+        for v in variants:
+            keys = [(kbs[k], kd.galois, kd.seed if v == "regen" else None, kas[k] if v == "stored" else None)
+                    for k, kd in enumerate(d.keys)]
+            fn = lambda i, keys=keys: ctx.keyswitch_hoisted(ct, LEVEL, keys, out=out)
+            ms = time_calls(fn, args.steps, args.warmup, torch)
+            ctx.profile(True)
+            for i in range(args.steps):
+                fn(i)
+            ctx.profile(False)
+            prof = ctx.profile_read()
+            res[v] = {"key_switches_per_s": round(16 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                      "hbm_roofline_frac": round(hbm_bytes(LEVEL, 1, v == "regen", 16) / (ms * 1e-3) / HBM_PEAK, 4),
+                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+    else:
+        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=1)
+        kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
+        kas = [ctx.expand_a(kd.seed) for kd in d.keys] if "stored" in variants else None
+        cts = [to_device(c[None]) for c in d.cts]
+        outs = [torch.empty((1, 2, lv, N), dtype=torch.int32, device="cuda") for lv in d.levels]
+        for v in variants:
+            def stream(i, v=v):
+                for c in range(len(cts)):
+                    k = d.key_index[c]
+                    ctx.keyswitch(cts[c], d.levels[c], kbs[k], wl.galois[k],
+                                  key_seed=d.keys[k].seed if v == "regen" else None,
+                                  key_a=kas[k] if v == "stored" else None, out=outs[c])
+            ms = time_calls(stream, args.steps, args.warmup, torch)
+            byts = sum(hbm_bytes(lv, 1, v == "regen") for lv in d.levels)
+            res[v] = {"key_switches_per_s": round(len(cts) / (ms * 1e-3), 1), "ms_per_stream": round(ms, 4),
+                      "hbm_roofline_frac": round(byts / (ms * 1e-3) / HBM_PEAK, 4)}
+        res["key_set_bytes"] = {"regen": len(d.keys) * DNUM * (L + K) * N * 4,
+                                "stored": 2 * len(d.keys) * DNUM * (L + K) * N * 4}
+    print(json.dumps(res))
     ctx.close()
     return 0
 

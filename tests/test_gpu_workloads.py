@@ -1,0 +1,88 @@
+"""GPU parity on the shapes of the level sweep, the hoisted 16-key stage and the mixed decode stream.
+
+Each run executes the whole workload on the GPU in the launch configuration the
+benchmark times; sampled outputs are compared bit-exactly with the oracle.  Key
+b-halves are uniform residues (the same distribution as a real b-half): the bits
+of the output do not depend on whether the key is a valid encryption.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+from tests.gpu_common import announce, context, first_mismatch, gpu, host, params
+
+pytestmark = pytest.mark.gpu
+
+from oracle import ks as oks  # noqa: E402
+from oracle.chacha import expand_key_a  # noqa: E402
+from rns_ckks_key_amd import synth  # noqa: E402
+
+
+@functools.lru_cache(maxsize=None)
+def key_rows(seed_int: int):
+    pr = params("boot")
+    return synth.uniform_key_rows(seed_int, pr.primes, pr.dnum, pr.n).astype(np.uint64)
+
+
+@functools.lru_cache(maxsize=None)
+def key_a(seed: bytes):
+    pr = params("boot")
+    return expand_key_a(seed, pr.primes, pr.dnum, pr.n)
+
+
+def test_level_sweep_batch16():
+    # workload 3: batch 16 at levels 36, 24, 12, 4 under workload 2's key
+    pr = params("boot")
+    ctx = context("boot", 16)
+    d = synth.draw(3, pr.primes)
+    seed = d.keys[0].seed
+    kb = key_rows(3003)
+    dkb = gpu(kb)
+    for li, level in enumerate(synth.WORKLOADS[3].levels):
+        announce(f"level sweep level={level}")
+        cts = np.stack(d.cts[16 * li:16 * li + 16])
+        got = host(ctx.keyswitch(gpu(cts), level, dkb, 5, key_seed=seed))
+        b = [15, 7, 0, 9][li]
+        want = oks.keyswitch(pr, cts[b].astype(np.uint64), level, kb, 5, key_a=key_a(seed))
+        assert np.array_equal(got[b], want), (level, b, first_mismatch(got[b], want))
+
+
+def test_hoisted_sixteen_keys():
+    # workload 4: one ciphertext at level 36, 16 keys g = 5^k with their own seeds, one hoisted call
+    announce("hoisted 16 keys")
+    pr = params("boot")
+    ctx = context("boot", 16)
+    d = synth.draw(4, pr.primes)
+    ct = d.cts[0]
+    keys = []
+    for k, kd in enumerate(d.keys):
+        keys.append((gpu(key_rows(4000 + k)), kd.galois, kd.seed, None))
+    got = host(ctx.keyswitch_hoisted(gpu(ct), 36, keys))
+    for k in (0, 9, 15):
+        kd = d.keys[k]
+        want = oks.keyswitch(pr, ct.astype(np.uint64), 36, key_rows(4000 + k), kd.galois, key_a=key_a(kd.seed))
+        assert np.array_equal(got[k], want), (k, first_mismatch(got[k], want))
+
+
+def test_mixed_stream_sixty_four():
+    # workload 5: 64 ciphertexts, levels 8..36, each under one of 33 keys; one call per ciphertext
+    announce("mixed stream 64")
+    pr = params("boot")
+    ctx = context("boot", 16)
+    d = synth.draw(5, pr.primes)
+    wl = synth.WORKLOADS[5]
+    dkb = {}
+    outs = []
+    for i, ct in enumerate(d.cts):
+        k = d.key_index[i]
+        if k not in dkb:
+            dkb[k] = gpu(key_rows(5000 + k))
+        lvl = d.levels[i]
+        outs.append(ctx.keyswitch(gpu(ct[None]), lvl, dkb[k], wl.galois[k], key_seed=d.keys[k].seed))
+    for i in (0, 31, 63):
+        k, lvl = d.key_index[i], d.levels[i]
+        got = host(outs[i])[0]
+        want = oks.keyswitch(pr, d.cts[i].astype(np.uint64), lvl, key_rows(5000 + k), wl.galois[k],
+                             key_a=key_a(d.keys[k].seed))
+        assert np.array_equal(got, want), (i, lvl, k, first_mismatch(got, want))
