@@ -72,6 +72,7 @@ struct ConvArgs {
   uint32_t n_targets;        // targets e; dst limb = e < skip_lo ? e : e + ns; abs prime via level map
   uint32_t skip;             // 1: skip the source limbs' own range in the destination limbs
   uint32_t level;            // ext mapping: dlimb < level ? dlimb : L + dlimb - level (level=0: dlimb)
+  uint32_t tchunks;          // targets split over this many workgroups (set by the launcher)
 };
 
 struct KeyRef {
