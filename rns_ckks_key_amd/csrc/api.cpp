@@ -387,7 +387,7 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
 // Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (ctx->ext already filled).
 hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
                           uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
-                          hipStream_t s) {
+                          bool digits_ntt, hipStream_t s) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::IpArgs ip{};
@@ -402,6 +402,7 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   ip.conv = c->conv;
   ip.out = out;
   ip.regen_blocks = c->regen_blocks;
+  ip.digits_ntt = digits_ntt ? 1u : 0u;
   ip.n_keys = n_keys;
   for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
   hipError_t e;
@@ -740,7 +741,7 @@ ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t leve
   if (!key_a) seed_words(key_seed, k.seed);
   k.galois = galois_elt;
   e = run_ip_moddown(c, ct, 2ull * level * N, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k,
-                     out, s);
+                     out, false, s);
   return hip_status(e, "inner product / ModDown");
 }
 
@@ -764,6 +765,26 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
   const uint64_t N = c->h.n;
   hipError_t e = run_modup(c, ct + (uint64_t)level * N, 0, level, 1, s);
   if (e != hipSuccess) return hip_status(e, "ModUp");
+  // the digits are shared by every key: finish their NTT once (row half, own limbs copied from c1)
+  const Host& h = c->h;
+  for (uint32_t j = 0; j < digits_at(h, level); ++j) {
+    ckks::RowArgs r{};
+    r.src = c->ext + (uint64_t)j * (h.L + h.K) * N;
+    r.dst = c->ext + (uint64_t)j * (h.L + h.K) * N;
+    r.src_item_stride = r.dst_item_stride = 0;
+    r.prime0 = 0;
+    r.n_limbs = level + h.K;
+    r.own_lo = j * h.alpha;
+    r.own_n = std::min(h.alpha, level - j * h.alpha);
+    r.own_src = ct + (uint64_t)level * N;
+    r.own_item_stride = 0;
+    r.level = level;
+    {
+      ProfScope p(c, CKKS_K_ROW, s);
+      e = ckks::launch_row(c->d, r, true, 1, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "digit row pass");
+  }
   const uint32_t chunk = std::min<uint32_t>(c->max_batch, 16);
   for (uint32_t k0 = 0; k0 < n_keys; k0 += chunk) {
     const uint32_t nk = std::min(chunk, n_keys - k0);
@@ -775,7 +796,7 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
       if (!keys[k].a) seed_words(key_seeds + 32 * (k0 + k), keys[k].seed);
       keys[k].galois = galois_elts[k0 + k];
     }
-    e = run_ip_moddown(c, ct, 0, 0, level, 1, nk, keys, out + (uint64_t)k0 * 2 * level * N, s);
+    e = run_ip_moddown(c, ct, 0, 0, level, 1, nk, keys, out + (uint64_t)k0 * 2 * level * N, true, s);
     if (e != hipSuccess) return hip_status(e, "inner product / ModDown");
   }
   return ok();

@@ -94,6 +94,7 @@ struct IpArgs {
   const uint32_t* conv;      // final input   [item][2][level][N] (row pass pending)
   uint32_t* out;             // final output  [item][2][level][N]
   uint32_t regen_blocks;
+  uint32_t digits_ntt;       // 1: ext holds fully transformed digits, own limbs included (hoisted calls)
   uint32_t n_keys;
   KeyRef key[16];            // per key group (grid z)
 };
