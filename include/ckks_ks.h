@@ -128,6 +128,26 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx *ctx, const uint32_t *ct, uint
                                    const uint32_t *const *key_a, const uint32_t *galois_elts,
                                    uint32_t *out, void *stream);
 
+/* One ciphertext of a multi-item call: its own level, key and Galois element. */
+typedef struct {
+  const uint32_t *ct;        /* [2][level][N], NTT domain (device) */
+  uint32_t *out;             /* [2][level][N] (device), must not alias any input */
+  const uint32_t *key_b;     /* [dnum][L+K][N] (device) */
+  const uint32_t *key_a;     /* stored a-half (device) or NULL: regenerate from key_seed */
+  uint8_t key_seed[32];      /* ChaCha12 seed of the a-half, used when key_a is NULL */
+  uint32_t level;            /* 1..L */
+  uint32_t galois_elt;       /* odd, < 2N */
+} ckks_ks_item;
+
+/* A stream of independent key-switches (different levels, keys and Galois
+ * elements), bit-identical to one ckks_keyswitch call per item with batch 1.
+ * Items of equal level are processed together, up to min(16, max_batch) per
+ * launch sequence, so a decode-shaped stream does not pay one small launch
+ * sequence per ciphertext.  items is a host array.  Errors: EINVAL (NULL
+ * pointers), ERANGE (an item's level or Galois element), with the item index in
+ * ckks_last_error(); nothing is launched if any item is invalid. */
+ckks_status ckks_keyswitch_multi(const ckks_ctx *ctx, uint32_t n_items, const ckks_ks_item *items, void *stream);
+
 /* The a-half [dnum][L+K][N] that key_seed (host, 32 bytes) regenerates: the stored
  * variant of a key.  Stream layout: one ChaCha12 sub-stream per (digit j,
  * absolute prime t, tile tau of 1024 coefficients); state = "expand 32-byte k",

@@ -36,6 +36,13 @@ PU32 = ctypes.POINTER(ctypes.c_uint32)
 PU64 = ctypes.POINTER(ctypes.c_uint64)
 PCTX = ctypes.c_void_p
 
+class KsItem(ctypes.Structure):
+    """ckks_ks_item of include/ckks_ks.h."""
+    _fields_ = [("ct", ctypes.c_void_p), ("out", ctypes.c_void_p), ("key_b", ctypes.c_void_p),
+                ("key_a", ctypes.c_void_p), ("key_seed", ctypes.c_uint8 * 32), ("level", ctypes.c_uint32),
+                ("galois_elt", ctypes.c_uint32)]
+
+
 _SIGS = {
     "ckks_last_error": (ctypes.c_char_p, []),
     "ckks_chain_primes": (ctypes.c_int, [U32, U32, U32, PU32]),
@@ -50,6 +57,7 @@ _SIGS = {
     "ckks_keyswitch_hoisted": (ctypes.c_int, [PCTX, P, U32, U32, ctypes.POINTER(P), ctypes.c_char_p,
                                               ctypes.POINTER(P), PU32, P, P]),
     "ckks_expand_a": (ctypes.c_int, [PCTX, ctypes.c_char_p, P, P]),
+    "ckks_keyswitch_multi": (ctypes.c_int, [PCTX, U32, ctypes.POINTER(KsItem), P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
     "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
     "ckks_profile_read": (ctypes.c_int, [PCTX, ctypes.POINTER(ctypes.c_double), PU32, U32]),

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import KERNEL_CLASSES, PCTX, U32, U64, CkksError, check, lib
+from ._lib import KERNEL_CLASSES, PCTX, U32, U64, CkksError, KsItem, check, lib
 
 __all__ = ["Context", "CkksError", "chain_primes", "to_device", "to_numpy"]
 
@@ -169,6 +169,29 @@ class Context:
         check(lib.ckks_keyswitch_hoisted(self._h, _ptr(ct, (2, level, self.n), "ct"), level, nk, kb, seeds, ka,
                                          gal, _ptr(out, (nk, 2, level, self.n), "out"), _stream()))
         return out
+
+    def keyswitch_multi(self, items: list) -> list:
+        """items: list of (ct [2][l][N], level, key_b, galois, key_seed or None, key_a or None, out or None).
+
+        One key-switch per item, bit-identical to separate keyswitch calls; returns the outputs."""
+        kshape = (self.dnum, self.L + self.K, self.n)
+        arr = (KsItem * len(items))()
+        outs = []
+        for i, (ct, level, key_b, galois, seed, key_a, out) in enumerate(items):
+            if out is None:
+                out = torch.empty((2, level, self.n), dtype=torch.int32, device=ct.device)
+            outs.append(out)
+            it = arr[i]
+            it.ct = _ptr(ct, (2, level, self.n), "ct")
+            it.out = _ptr(out, (2, level, self.n), "out")
+            it.key_b = _ptr(key_b, kshape, "key_b")
+            it.key_a = _ptr(key_a, kshape, "key_a") if key_a is not None else None
+            if key_a is None:
+                ctypes.memmove(it.key_seed, _seed(seed), 32)
+            it.level = level
+            it.galois_elt = galois
+        check(lib.ckks_keyswitch_multi(self._h, len(items), arr, _stream()))
+        return outs
 
     def expand_a(self, seed: bytes, out: torch.Tensor | None = None, device="cuda") -> torch.Tensor:
         kshape = (self.dnum, self.L + self.K, self.n)

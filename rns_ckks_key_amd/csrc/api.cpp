@@ -341,11 +341,15 @@ uint32_t digits_at(const Host& h, uint32_t level) { return (level + h.alpha - 1)
 
 // Steps 1-2: INTT row half of c1 and the fused ModUp conversion into ctx->ext.
 hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, uint32_t level, uint32_t items,
-                     hipStream_t s) {
+                     hipStream_t s, const uint32_t* const* c1_items = nullptr) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::RowArgs r{};
   r.src = c1;
+  if (c1_items) {  // one pointer per item (at most kMaxGroup)
+    r.use_srcs = 1;
+    for (uint32_t i = 0; i < items; ++i) r.srcs[i] = c1_items[i];
+  }
   r.dst = c->rowtmp;
   r.src_item_stride = c1_item_stride;
   r.dst_item_stride = (uint64_t)level * N;
@@ -387,7 +391,7 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
 // Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (ctx->ext already filled).
 hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
                           uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
-                          bool digits_ntt, hipStream_t s) {
+                          bool digits_ntt, hipStream_t s, bool per_group = false) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::IpArgs ip{};
@@ -403,6 +407,7 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   ip.out = out;
   ip.regen_blocks = c->regen_blocks;
   ip.digits_ntt = digits_ntt ? 1u : 0u;
+  ip.per_group = per_group ? 1u : 0u;
   ip.n_keys = n_keys;
   for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
   hipError_t e;
@@ -785,10 +790,10 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
     }
     if (e != hipSuccess) return hip_status(e, "digit row pass");
   }
-  const uint32_t chunk = std::min<uint32_t>(c->max_batch, 16);
+  const uint32_t chunk = std::min<uint32_t>(c->max_batch, ckks::kMaxGroup);
   for (uint32_t k0 = 0; k0 < n_keys; k0 += chunk) {
     const uint32_t nk = std::min(chunk, n_keys - k0);
-    ckks::KeyRef keys[16];
+    ckks::KeyRef keys[ckks::kMaxGroup];
     for (uint32_t k = 0; k < nk; ++k) {
       keys[k] = ckks::KeyRef{};
       keys[k].b = key_b[k0 + k];
@@ -798,6 +803,59 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
     }
     e = run_ip_moddown(c, ct, 0, 0, level, 1, nk, keys, out + (uint64_t)k0 * 2 * level * N, true, s);
     if (e != hipSuccess) return hip_status(e, "inner product / ModDown");
+  }
+  return ok();
+}
+
+ckks_status ckks_keyswitch_multi(const ckks_ctx* cc, uint32_t n_items, const ckks_ks_item* items, void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (n_items == 0) return ok();
+  if (!items) return fail(CKKS_EINVAL, "items is NULL");
+  for (uint32_t i = 0; i < n_items; ++i) {
+    const ckks_ks_item& it = items[i];
+    if (!it.ct || !it.out || !it.key_b) return fail(CKKS_EINVAL, "item %u: ct, out or key_b is NULL", i);
+    if ((st = check_level(c, it.level)) || (st = check_galois(c, it.galois_elt))) {
+      std::string m = g_err;
+      return fail(st, "item %u: %s", i, m.c_str());
+    }
+  }
+  if ((st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  const uint32_t chunk = std::min<uint32_t>(c->max_batch, ckks::kMaxGroup);
+  // items of one level run together: one ModUp batch, then the key-using kernels over all their keys
+  std::vector<bool> done(n_items, false);
+  for (uint32_t i0 = 0; i0 < n_items; ++i0) {
+    if (done[i0]) continue;
+    const uint32_t level = items[i0].level;
+    std::vector<uint32_t> group;
+    for (uint32_t i = i0; i < n_items; ++i)
+      if (!done[i] && items[i].level == level) group.push_back(i);
+    for (size_t g0 = 0; g0 < group.size(); g0 += chunk) {
+      const uint32_t m = (uint32_t)std::min<size_t>(chunk, group.size() - g0);
+      const uint32_t* c1s[ckks::kMaxGroup];
+      ckks::KeyRef keys[ckks::kMaxGroup];
+      for (uint32_t k = 0; k < m; ++k) {
+        const ckks_ks_item& it = items[group[g0 + k]];
+        done[group[g0 + k]] = true;
+        c1s[k] = it.ct + (uint64_t)level * N;
+        keys[k] = ckks::KeyRef{};
+        keys[k].b = it.key_b;
+        keys[k].a = it.key_a;
+        if (!it.key_a) seed_words(it.key_seed, keys[k].seed);
+        keys[k].galois = it.galois_elt;
+        keys[k].ct = it.ct;
+        keys[k].out = it.out;
+      }
+      hipError_t e = run_modup(c, nullptr, 0, level, m, s, c1s);
+      if (e != hipSuccess) return hip_status(e, "ModUp");
+      e = run_ip_moddown(c, nullptr, 0, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, m, keys, nullptr, false, s,
+                         true);
+      if (e != hipSuccess) return hip_status(e, "inner product / ModDown");
+    }
   }
   return ok();
 }

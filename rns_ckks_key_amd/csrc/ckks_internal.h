@@ -34,10 +34,14 @@ struct DevTables {
 };
 
 // Row pass over limbs: blocks of 1024 coefficients, one wave per block.
+constexpr uint32_t kMaxGroup = 16;     // items whose pointers travel in kernel arguments
+
 struct RowArgs {
   const uint32_t* src;
   uint32_t* dst;
   uint64_t src_item_stride, dst_item_stride;   // words between items
+  const uint32_t* srcs[kMaxGroup];             // per-item sources (when use_srcs)
+  uint32_t use_srcs;
   uint32_t prime0;           // absolute prime of limb 0
   uint32_t n_limbs;
   // ModUp finish mode: limbs [own_lo, own_lo+own_n) are copied from `own_src` untransformed
@@ -80,6 +84,8 @@ struct KeyRef {
   const uint32_t* a;         // stored a-half or nullptr
   uint32_t seed[8];
   uint32_t galois;
+  const uint32_t* ct;        // per-group ciphertext [2][level][N] (per_group mode)
+  uint32_t* out;             // per-group output [2][level][N] (per_group mode)
 };
 
 // Inner product (+ fused ModDown pieces).  Grid: x = limb, y = 1024-block, z = key group.
@@ -95,8 +101,10 @@ struct IpArgs {
   uint32_t* out;             // final output  [item][2][level][N]
   uint32_t regen_blocks;
   uint32_t digits_ntt;       // 1: ext holds fully transformed digits, own limbs included (hoisted calls)
+  uint32_t per_group;        // 1: key group g has its own ciphertext key[g].ct, output key[g].out and
+                             //    digits at ext + g * ext_ct_stride (n_ct = 1)
   uint32_t n_keys;
-  KeyRef key[16];            // per key group (grid z)
+  KeyRef key[kMaxGroup];     // per key group (grid z)
 };
 
 hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t items, hipStream_t s);

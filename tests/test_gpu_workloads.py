@@ -86,3 +86,34 @@ def test_mixed_stream_sixty_four():
         want = oks.keyswitch(pr, d.cts[i].astype(np.uint64), lvl, key_rows(5000 + k), wl.galois[k],
                              key_a=key_a(d.keys[k].seed))
         assert np.array_equal(got, want), (i, lvl, k, first_mismatch(got, want))
+
+
+def test_multi_item_equals_single_calls():
+    # ckks_keyswitch_multi over the mixed stream (levels repeat, keys differ, stored and regenerated mixed)
+    # is bit-identical to one ckks_keyswitch call per item; two items are checked against the oracle
+    announce("multi-item stream")
+    pr = params("boot")
+    ctx = context("boot", 16)
+    d = synth.draw(5, pr.primes)
+    wl = synth.WORKLOADS[5]
+    dkb, dka, items = {}, {}, []
+    for i, ct in enumerate(d.cts):
+        k = d.key_index[i]
+        if k not in dkb:
+            dkb[k] = gpu(key_rows(5000 + k))
+        stored = (i % 3 == 1)
+        if stored and k not in dka:
+            dka[k] = ctx.expand_a(d.keys[k].seed)
+        items.append((gpu(ct), d.levels[i], dkb[k], wl.galois[k], None if stored else d.keys[k].seed,
+                      dka[k] if stored else None, None))
+    outs = ctx.keyswitch_multi(items)
+    for i in range(len(items)):
+        ct, lvl, kb, g, seed, ka, _ = items[i]
+        single = ctx.keyswitch(ct[None], lvl, kb, g, key_seed=seed, key_a=ka)
+        a, b = host(outs[i]), host(single)[0]
+        assert np.array_equal(a, b), (i, lvl, first_mismatch(a, b))
+    for i in (5, 40):
+        k, lvl = d.key_index[i], d.levels[i]
+        want = oks.keyswitch(pr, d.cts[i].astype(np.uint64), lvl, key_rows(5000 + k), wl.galois[k],
+                             key_a=key_a(d.keys[k].seed))
+        assert np.array_equal(host(outs[i]), want), (i, first_mismatch(host(outs[i]), want))
