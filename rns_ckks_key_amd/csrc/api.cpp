@@ -122,7 +122,8 @@ uint32_t r64(uint32_t q) {  // 2^64 mod q
 struct Host {
   uint32_t log_n = 0, n = 0, L = 0, K = 0, dnum = 0, alpha = 0;
   std::vector<uint32_t> q, qinv, psi;
-  std::vector<uint2> tw, itw, ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one;
+  std::vector<uint32_t> tw, itw;
+  std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one;
   std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound;
 };
 
@@ -148,8 +149,8 @@ void build_tables(Host& h) {
     }
     for (uint32_t k = 0; k < n; ++k) {
       const uint32_t r = brv(k, h.log_n);
-      h.tw[(size_t)t * n + k] = mont(pw[r], q);
-      h.itw[(size_t)t * n + k] = mont(ipw[r], q);
+      h.tw[(size_t)t * n + k] = mont(pw[r], q).x;
+      h.itw[(size_t)t * n + k] = mont(ipw[r], q).x;
     }
     h.ninv[t] = mont(invmod(n % q, q), q);
     h.bound[t] = (uint32_t)(((1ull << 32) / q) * q);

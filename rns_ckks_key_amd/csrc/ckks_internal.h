@@ -18,8 +18,8 @@ struct DevTables {
   uint32_t log_n, n, L, K, dnum, alpha;
   const uint32_t* q;        // [L+K]
   const uint32_t* qinv;     // [L+K] q^-1 mod 2^32
-  const uint2* tw;          // [L+K][N]  psi^brv(k)
-  const uint2* itw;         // [L+K][N]  psi^-brv(k)
+  const uint32_t* tw;       // [L+K][N]  psi^brv(k) * 2^32 mod q (companion computed on use)
+  const uint32_t* itw;      // [L+K][N]  psi^-brv(k) * 2^32 mod q
   const uint2* ninv;        // [L+K]     N^-1
   const uint2* mu_scale;    // [L+1][L]  N^-1 * (Qd/q_i)^-1 mod q_i for i's digit at level l
   const uint32_t* mu_conv;  // [L+1][dnum][alpha][L+K]  (Qd/q_i) * 2^64 mod q_t (plain)
