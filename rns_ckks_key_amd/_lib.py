@@ -27,6 +27,11 @@ class CkksError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m rns_ckks_key_amd.build` (hipcc, gfx950)")
 
+# torch brings its own HIP runtime under the same soname as the one the library
+# links.  Loading torch first makes the library bind to that single runtime; the
+# other order puts two HIP runtimes in the process and device calls then fail.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 P = ctypes.c_void_p

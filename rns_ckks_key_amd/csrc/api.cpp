@@ -508,9 +508,9 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
     *out = c;
     return ok();
   }
-  if (hipGetDevice(&c->device) != hipSuccess) {
+  if (const hipError_t e = hipGetDevice(&c->device); e != hipSuccess) {
     delete c;
-    return fail(CKKS_EHIP, "hipGetDevice failed (no GPU?)");
+    return fail(CKKS_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   }
   ckks_status st = upload_tables(c);
   if (st != CKKS_OK) {

@@ -114,3 +114,33 @@ def test_repeatable_and_stream_ordered():
         out = ctx.keyswitch(ct, 5, kb, 25, key_seed=seed)
     side.synchronize()
     assert np.array_equal(host(out), first)
+
+
+@functools.lru_cache(maxsize=None)
+def setup_wide():
+    shape = (12, 8, 2, 8, 30)  # dnum = 8, the largest digit count: eight key tiles per workgroup
+    pr = Params.make(*shape)
+    return pr, Context(shape[0], shape[1], shape[2], shape[3], pr.primes, 12)
+
+
+@pytest.mark.parametrize("batch", [4, 5, 8, 12])
+def test_keyswitch_batches_eight_digits(batch):
+    # batches of 4..7 and of 8 or more take the multi-wave inner-product kernels;
+    # eight digits make the regenerated tiles span more than one pass of the workgroup
+    announce(f"keyswitch dnum 8 batch {batch}")
+    pr, ctx = setup_wide()
+    rng = np.random.default_rng(100 + batch)
+    g = 3 ** 5 % (2 * pr.n)
+    s = synth.ternary(rng, pr.n)
+    s_src = oks.rotation_source(s, g, pr)
+    errs = [synth.gaussian(rng, pr.n) for _ in range(pr.dnum)]
+    seed = rng.bytes(32)
+    kb, ka = oks.keygen(pr, s, s_src, errs, seed)
+    dkb, dka = gpu(kb), gpu(ka)
+    for level in (pr.L, 5):
+        ct = np.stack([np.stack([rand_limbs(rng, pr.primes[:level], pr.n) for _ in range(2)]) for _ in range(batch)])
+        want = oks.keyswitch(pr, ct, level, kb, g, key_a=ka)
+        for variant in ("regen", "stored"):
+            got = host(ctx.keyswitch(gpu(ct), level, dkb, g, key_seed=seed if variant == "regen" else None,
+                                     key_a=dka if variant == "stored" else None))
+            assert np.array_equal(got, want), (variant, level, first_mismatch(got, want))
