@@ -155,8 +155,8 @@ def cpu_baseline(primes, draw, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5], default=2,
@@ -271,9 +271,11 @@ def main() -> int:
     out["config"]["variant"] = head_name
     if "stored" in res and head_name != "stored":
         st = res["stored"]
+        sp = st["prof"]
         out["stored_key"] = {"value": round(st["key_switches_per_s"], 1), "ms_per_step": round(st["ms_per_step"], 4),
                              "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, False) / (st["ms_per_step"] * 1e-3)
-                                                        / HBM_PEAK, 4)}
+                                                        / HBM_PEAK, 4),
+                             "kernel_ms_per_call": {k: round(sp[k][0] / args.steps, 4) for k in sp if sp[k][1]}}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(primes, {"cts": cts, "key_b": kb_host, "seed": seed}, args.cpu_budget)
     print(json.dumps(out))
