@@ -156,6 +156,32 @@ ckks_status ckks_keyswitch_multi(const ckks_ctx *ctx, uint32_t n_items, const ck
  * and gives w mod q_t; the k-th accepted word is coefficient tau*1024 + k. */
 ckks_status ckks_expand_a(const ckks_ctx *ctx, const uint8_t *key_seed, uint32_t *key_a, void *stream);
 
+/* Rescale by the last active prime: out[batch][2][level-1][N] from
+ * ct[batch][2][level][N], both NTT domain, level >= 2.  With the floor convention
+ * of ModDown: c_i <- (c_i - NTT_i([INTT_{q_{l-1}}(c_{l-1})] mod q_i)) * q_{l-1}^-1
+ * mod q_i for i < l-1, so a coefficient C in [0, Q_l) becomes floor(C / q_{l-1}).
+ * The pages name rescaling only as the multiplication depth a CKKS ciphertext
+ * spends (EncryptedLLM summary on lpnh, "Core problem" paragraph); the RNS steps
+ * are those of Cheon et al., SAC 2018.  out must not overlap ct.
+ * Errors: EINVAL (NULL, overlap), ERANGE (level outside 2..L, batch). */
+ckks_status ckks_rescale(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, uint32_t *out, uint32_t batch,
+                         void *stream);
+
+/* Multiply, relinearise and rescale: out[batch][2][level-1][N] =
+ * Rescale(e0, e1) with (d0, d1, d2) = x (x) y, the NTT-domain tensor product
+ * (d0 = x0*y0, d1 = x0*y1 + x1*y0, d2 = x1*y1 mod q_i), and (e0, e1) =
+ * (d0 + ModDown(acc_b), d1 + ModDown(acc_a)) the key-switch of d2 (ModUp, inner
+ * product, ModDown exactly as ckks_keyswitch with Galois element 1).  The key
+ * (key_b, and key_a or key_seed as in ckks_keyswitch) switches from s^2 to s.
+ * x, y: [batch][2][level][N]; level >= 2.  Relinearisation is one of the
+ * key-switches whose key the pages regenerate in-kernel (Perseus summary on
+ * ai4snews, "Interpretation" paragraph 2).  Uses the context's workspace (the
+ * tensor product needs 3*batch*level*N words of it).
+ * Errors: EINVAL (NULL, no key_a or seed), ERANGE (level outside 2..L, batch). */
+ckks_status ckks_mul_relin_rescale(const ckks_ctx *ctx, const uint32_t *x, const uint32_t *y, uint32_t level,
+                                   const uint32_t *key_b, const uint8_t *key_seed, const uint32_t *key_a,
+                                   uint32_t *out, uint32_t batch, void *stream);
+
 /* Test knob: number of ChaCha blocks generated per 1024-word tile before the
  * rare continuation path runs (default 68, at least 64).  64 sends every tile
  * with a rejected word through the continuation path. */
@@ -171,7 +197,10 @@ typedef enum {
   CKKS_K_IP_FINAL = 5,     /* inner product over the ciphertext primes + end of ModDown */
   CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
   CKKS_K_MODDOWN_FINAL = 7,/* end of the standalone ModDown */
-  CKKS_K_CLASSES = 8
+  CKKS_K_TENSOR = 8,       /* tensor product of two ciphertexts */
+  CKKS_K_RESCALE_CONV = 9, /* column INTT of the dropped limb, its reduction and column NTT */
+  CKKS_K_RESCALE_FINAL = 10,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
+  CKKS_K_CLASSES = 11
 } ckks_kernel_class;
 
 /* Measurement aid: while enabled, every launch of this context is bracketed by

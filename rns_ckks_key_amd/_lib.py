@@ -63,12 +63,15 @@ _SIGS = {
                                               ctypes.POINTER(P), PU32, P, P]),
     "ckks_expand_a": (ctypes.c_int, [PCTX, ctypes.c_char_p, P, P]),
     "ckks_keyswitch_multi": (ctypes.c_int, [PCTX, U32, ctypes.POINTER(KsItem), P]),
+    "ckks_rescale": (ctypes.c_int, [PCTX, P, U32, P, U32, P]),
+    "ckks_mul_relin_rescale": (ctypes.c_int, [PCTX, P, P, U32, P, ctypes.c_char_p, P, P, U32, P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
     "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
     "ckks_profile_read": (ctypes.c_int, [PCTX, ctypes.POINTER(ctypes.c_double), PU32, U32]),
 }
 
-KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final"]
+KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final",
+                  "tensor", "rescale_conv", "rescale_final"]
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

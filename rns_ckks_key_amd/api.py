@@ -193,6 +193,29 @@ class Context:
         check(lib.ckks_keyswitch_multi(self._h, len(items), arr, _stream()))
         return outs
 
+    def rescale(self, ct: torch.Tensor, level: int, out: torch.Tensor | None = None) -> torch.Tensor:
+        """[batch][2][level][N] -> [batch][2][level-1][N]: drop the last active prime (floor convention)."""
+        b = ct.shape[0]
+        if out is None:
+            out = torch.empty((b, 2, level - 1, self.n), dtype=torch.int32, device=ct.device)
+        check(lib.ckks_rescale(self._h, _ptr(ct, (b, 2, level, self.n), "ct"), level,
+                               _ptr(out, (b, 2, level - 1, self.n), "out"), b, _stream()))
+        return out
+
+    def mul_relin_rescale(self, x: torch.Tensor, y: torch.Tensor, level: int, key_b: torch.Tensor,
+                          key_seed: bytes | None = None, key_a: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+        """Rescale(Relinearise(x (x) y)) with the s^2 -> s key: [batch][2][level-1][N]."""
+        b = x.shape[0]
+        kshape = (self.dnum, self.L + self.K, self.n)
+        if out is None:
+            out = torch.empty((b, 2, level - 1, self.n), dtype=torch.int32, device=x.device)
+        check(lib.ckks_mul_relin_rescale(self._h, _ptr(x, (b, 2, level, self.n), "x"),
+                                         _ptr(y, (b, 2, level, self.n), "y"), level, _ptr(key_b, kshape, "key_b"),
+                                         _seed(key_seed), _ptr(key_a, kshape, "key_a"),
+                                         _ptr(out, (b, 2, level - 1, self.n), "out"), b, _stream()))
+        return out
+
     def expand_a(self, seed: bytes, out: torch.Tensor | None = None, device="cuda") -> torch.Tensor:
         kshape = (self.dnum, self.L + self.K, self.n)
         if out is None:

@@ -123,8 +123,8 @@ struct Host {
   uint32_t log_n = 0, n = 0, L = 0, K = 0, dnum = 0, alpha = 0;
   std::vector<uint32_t> q, qinv, psi;
   std::vector<uint32_t> tw, itw;
-  std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one;
-  std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound;
+  std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one, r2, rs_inv;
+  std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound, r64tab;
 };
 
 void build_tables(Host& h) {
@@ -136,6 +136,8 @@ void build_tables(Host& h) {
   h.ninv.resize(E);
   h.bound.resize(E);
   h.one.resize(E);
+  h.r2.resize(E);
+  h.r64tab.resize(E);
   for (uint32_t t = 0; t < E; ++t) {
     const uint32_t q = h.q[t];
     h.qinv[t] = inv2_32(q);
@@ -155,7 +157,14 @@ void build_tables(Host& h) {
     h.ninv[t] = mont(invmod(n % q, q), q);
     h.bound[t] = (uint32_t)(((1ull << 32) / q) * q);
     h.one[t] = mont(1, q);
+    h.r2[t] = mont(r32(q), q);
+    h.r64tab[t] = r64(q);
   }
+  // rescale at level l: q_{l-1}^-1 mod q_i for i < l-1
+  h.rs_inv.assign((size_t)(L + 1) * L, make_uint2(0, 0));
+  for (uint32_t l = 2; l <= L; ++l)
+    for (uint32_t i = 0; i + 1 < l; ++i)
+      h.rs_inv[(size_t)l * L + i] = mont(invmod(h.q[l - 1] % h.q[i], h.q[i]), h.q[i]);
   // ModUp: per level l, digit j, source prime i of the digit, target prime t
   h.mu_scale.assign((size_t)(L + 1) * L, make_uint2(0, 0));
   h.mu_conv.assign((size_t)(L + 1) * h.dnum * A * E, 0);
@@ -230,6 +239,7 @@ struct ckks_ctx {
   uint32_t* ext = nullptr;     // [B][dnum][L+K][N]
   uint32_t* tmpP = nullptr;    // [B][2][K][N]
   uint32_t* conv = nullptr;    // [B][2][L][N]
+  uint32_t* tens = nullptr;    // [B][3][L][N]: tensor product (d0, d2 pair, then d1)
   // per-launch event timer (measurement aid)
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev;     // pool: 2 events per record
@@ -283,6 +293,9 @@ ckks_status upload_tables(ckks_ctx* c) {
       {h.md_fin_pl.data(), bytes_of(h.md_fin_pl), (const void**)&d.md_fin_pl},
       {h.bound.data(), bytes_of(h.bound), (const void**)&d.bound},
       {h.one.data(), bytes_of(h.one), (const void**)&d.one},
+      {h.r2.data(), bytes_of(h.r2), (const void**)&d.r2},
+      {h.r64tab.data(), bytes_of(h.r64tab), (const void**)&d.r64},
+      {h.rs_inv.data(), bytes_of(h.rs_inv), (const void**)&d.rs_inv},
   };
   size_t total = 0;
   for (auto& p : parts) total += (p.bytes + 255) & ~size_t(255);
@@ -392,7 +405,8 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
 // Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (ctx->ext already filled).
 hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
                           uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
-                          bool digits_ntt, hipStream_t s, bool per_group = false) {
+                          bool digits_ntt, hipStream_t s, bool per_group = false,
+                          const uint32_t* add_a = nullptr, uint64_t add_a_item = 0) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::IpArgs ip{};
@@ -411,6 +425,8 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   ip.per_group = per_group ? 1u : 0u;
   ip.n_keys = n_keys;
   for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
+  ip.add_a = add_a;
+  ip.add_a_item = add_a_item;
   hipError_t e;
   {
     ProfScope p(c, CKKS_K_IP_SPECIAL, s);
@@ -520,9 +536,9 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
     return st;
   }
   const uint64_t N = n, E = num_q + num_p, B = max_batch;
-  const uint64_t rowtmp = B * std::max(num_q, num_p) * N, ext = B * dnum * E * N, tmpP = B * 2 * num_p * N,
-                 conv = B * 2 * num_q * N;
-  c->ws_bytes = (rowtmp + ext + tmpP + conv) * sizeof(uint32_t);
+  const uint64_t rowtmp = B * std::max(std::max(num_q, num_p), 2u) * N, ext = B * dnum * E * N,
+                 tmpP = B * 2 * num_p * N, conv = B * 2 * num_q * N, tens = B * 3 * num_q * N;
+  c->ws_bytes = (rowtmp + ext + tmpP + conv + tens) * sizeof(uint32_t);
   if (hipMalloc(&c->ws, c->ws_bytes) != hipSuccess) {
     uint64_t b = c->ws_bytes;
     ckks_ctx_destroy(c);
@@ -532,6 +548,7 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
   c->ext = c->rowtmp + rowtmp;
   c->tmpP = c->ext + ext;
   c->conv = c->tmpP + tmpP;
+  c->tens = c->conv + conv;
   *out = c;
   return ok();
 }
@@ -749,6 +766,130 @@ ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t leve
   e = run_ip_moddown(c, ct, 2ull * level * N, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k,
                      out, false, s);
   return hip_status(e, "inner product / ModDown");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Rescale of `items` polynomials [level][N] (NTT domain), consecutive at stride level*N,
+// into out [level-1][N] at stride (level-1)*N: INTT of limb level-1 (row pass, then
+// the column pass inside the conversion kernel, which reduces it modulo each
+// q_i < q_{level-1} and applies the column NTT), then the row NTT fused with
+// (c_i - .) * q_{level-1}^-1.  Uses ctx->rowtmp and ctx->conv.
+hipError_t run_rescale(ckks_ctx* c, const uint32_t* src, uint32_t level, uint32_t* out, uint32_t items,
+                       hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  ckks::RowArgs r{};
+  r.src = src + (uint64_t)(level - 1) * N;
+  r.src_item_stride = (uint64_t)level * N;
+  r.dst = c->rowtmp;
+  r.dst_item_stride = N;
+  r.prime0 = level - 1;
+  r.n_limbs = 1;
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, false, items, s);
+  }
+  if (e != hipSuccess) return e;
+  ckks::ConvArgs a{};
+  a.src = c->rowtmp;
+  a.src_item = N;
+  a.src_y = 0;
+  a.dst = c->conv;
+  a.dst_item = (uint64_t)(level - 1) * N;
+  a.dst_y = 0;
+  a.src_prime0 = level - 1;
+  a.src_prime_step = 0;
+  a.ns_max = 1;
+  a.ns_limit = 1;
+  a.scale = c->d.ninv + (level - 1);  // the column INTT's N^-1; the source basis has one prime
+  a.scale_y = 0;
+  a.conv = c->d.r64;                  // z_i = x mod q_i (REDC2 leaves x * 2^64 * 2^-64)
+  a.conv_y = 0;
+  a.conv_s = 0;
+  a.conv_by_abs = 0;
+  a.n_targets = level - 1;
+  a.skip = 0;
+  a.level = level - 1;
+  {
+    ProfScope p(c, CKKS_K_RESCALE_CONV, s);
+    e = ckks::launch_conv(c->d, a, 1, items, s);
+  }
+  if (e != hipSuccess) return e;
+  ckks::RowArgs f{};
+  f.src = c->conv;
+  f.src_item_stride = (uint64_t)(level - 1) * N;
+  f.dst = out;
+  f.dst_item_stride = (uint64_t)(level - 1) * N;
+  f.prime0 = 0;
+  f.n_limbs = level - 1;
+  f.cmb = src;
+  f.cmb_item_stride = (uint64_t)level * N;
+  f.cmb_factor = c->d.rs_inv + (size_t)level * h.L;
+  ProfScope p(c, CKKS_K_RESCALE_FINAL, s);
+  return ckks::launch_row(c->d, f, true, items, s);
+}
+
+bool overlaps(const uint32_t* a, uint64_t na, const uint32_t* b, uint64_t nb) {
+  return a < b + nb && b < a + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+ckks_status ckks_rescale(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, uint32_t* out, uint32_t batch,
+                         void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!ct || !out) return fail(CKKS_EINVAL, "ct or out is NULL");
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch))) return st;
+  if (level < 2) return fail(CKKS_ERANGE, "rescale needs level >= 2 (got %u)", level);
+  const uint64_t N = c->h.n;
+  if (overlaps(ct, (uint64_t)batch * 2 * level * N, out, (uint64_t)batch * 2 * (level - 1) * N))
+    return fail(CKKS_EINVAL, "out overlaps ct");
+  if ((st = check_device(c))) return st;
+  return hip_status(run_rescale(c, ct, level, out, 2 * batch, (hipStream_t)stream), "rescale");
+}
+
+ckks_status ckks_mul_relin_rescale(const ckks_ctx* cc, const uint32_t* x, const uint32_t* y, uint32_t level,
+                                   const uint32_t* key_b, const uint8_t* key_seed, const uint32_t* key_a,
+                                   uint32_t* out, uint32_t batch, void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!x || !y || !key_b || !out) return fail(CKKS_EINVAL, "x, y, key_b or out is NULL");
+  if (!key_a && !key_seed) return fail(CKKS_EINVAL, "need key_a or key_seed");
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch))) return st;
+  if (level < 2) return fail(CKKS_ERANGE, "rescale needs level >= 2 (got %u)", level);
+  if ((st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t N = c->h.n, ln = (uint64_t)level * N;
+  uint32_t* pair = c->tens;                   // [B][2][l][N]: (d0, d2), later the relinearised (e0, e1)
+  uint32_t* d1 = c->tens + (uint64_t)batch * 2 * ln;  // [B][l][N]
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_TENSOR, s);
+    e = ckks::launch_tensor(c->d, x, y, pair, d1, level, batch, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "tensor product");
+  e = run_modup(c, pair + ln, 2 * ln, level, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  ckks::KeyRef k{};
+  k.b = key_b;
+  k.a = key_a;
+  if (!key_a) seed_words(key_seed, k.seed);
+  k.galois = 1;
+  // With Galois element 1 every final-pass workgroup reads c0, c1 and d1 only at the
+  // (limb, block) it writes, so the relinearised pair may overwrite (d0, d2) in place.
+  e = run_ip_moddown(c, pair, 2 * ln, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k, pair, false,
+                     s, false, d1, ln);
+  if (e != hipSuccess) return hip_status(e, "relinearisation");
+  return hip_status(run_rescale(c, pair, level, out, 2 * batch, s), "rescale");
 }
 
 ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, uint32_t n_keys,

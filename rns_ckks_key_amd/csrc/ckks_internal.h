@@ -31,6 +31,9 @@ struct DevTables {
   const uint2* md_fin_pl;   // [L] P^-1 mod q_i
   const uint32_t* bound;    // [L+K] floor(2^32/q)*q
   const uint2* one;         // [L+K] 1 (i.e. 2^32 mod q) for w mod q
+  const uint2* r2;          // [L+K] multiplier 2^32 mod q (undoes a Montgomery product's 2^-32)
+  const uint32_t* r64;      // [L+K] 2^64 mod q (plain): constant of a one-source reduction
+  const uint2* rs_inv;      // [L+1][L] q_{l-1}^-1 mod q_i (rescale at level l)
 };
 
 // Row pass over limbs: blocks of 1024 coefficients, one wave per block.
@@ -51,6 +54,10 @@ struct RowArgs {
   uint64_t own_item_stride;
   // ext-basis prime mapping (limb y -> absolute prime): y < level ? prime0 + y : L + (y - level)
   uint32_t level;            // 0: plain mapping prime0 + y
+  // forward pass only, when cmb != nullptr: dst = (cmb - NTT(src)) * cmb_factor[y]
+  const uint32_t* cmb;
+  uint64_t cmb_item_stride;
+  const uint2* cmb_factor;
 };
 
 // Column pass over limbs (in place): one thread per column of 2^(log_n-10) coefficients.
@@ -105,12 +112,16 @@ struct IpArgs {
                              //    digits at ext + g * ext_ct_stride (n_ct = 1)
   uint32_t n_keys;
   KeyRef key[kMaxGroup];     // per key group (grid z)
+  const uint32_t* add_a;     // optional [item][level][N] added to the final a-half output
+  uint64_t add_a_item;
 };
 
 hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t items, hipStream_t s);
 hipError_t launch_col(const DevTables& T, const ColArgs& a, bool fwd, bool scale_ninv, uint32_t items, hipStream_t s);
 hipError_t launch_conv(const DevTables& T, const ConvArgs& a, uint32_t groups, uint32_t items, hipStream_t s);
 hipError_t launch_ip(const DevTables& T, const IpArgs& a, bool final_pass, uint32_t n_limbs, hipStream_t s);
+hipError_t launch_tensor(const DevTables& T, const uint32_t* x, const uint32_t* y, uint32_t* pair, uint32_t* d1,
+                         uint32_t level, uint32_t items, hipStream_t s);
 hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
                          hipStream_t s);
 hipError_t launch_moddown_final(const DevTables& T, const uint32_t* x, uint64_t x_item, const uint32_t* conv,

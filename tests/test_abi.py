@@ -99,6 +99,21 @@ def test_host_context_validates_calls_before_any_launch():
     assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, None, None, gal, fake, None) == EINVAL
     assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, fake, None) == EINVAL
     assert lib.ckks_expand_a(h, None, fake, None) == EINVAL
+    far = ctypes.c_void_p(0x1000000)
+    assert lib.ckks_rescale(h, fake, 1, far, 1, None) == ERANGE  # nothing to drop at level 1
+    assert lib.ckks_rescale(h, fake, 5, far, 1, None) == ERANGE
+    assert lib.ckks_rescale(h, None, 4, far, 1, None) == EINVAL
+    assert lib.ckks_rescale(h, fake, 4, fake, 1, None) == EINVAL and "overlaps" in lib.ckks_last_error().decode()
+    assert lib.ckks_rescale(h, fake, 4, far, 1, None) == EINVAL and "host-only" in lib.ckks_last_error().decode()
+
+    def mrr(x=fake, level=4, kb=fake, sd=seed, ka=None, out=far, batch=1):
+        return lib.ckks_mul_relin_rescale(h, x, x, level, kb, sd, ka, out, batch, None)
+
+    assert mrr(level=1) == ERANGE
+    assert mrr(batch=0) == ERANGE
+    assert mrr(x=None) == EINVAL
+    assert mrr(sd=None) == EINVAL
+    assert mrr() == EINVAL and "host-only" in lib.ckks_last_error().decode()
     assert lib.ckks_ctx_set_regen_blocks(h, 63) == ERANGE
     assert lib.ckks_ctx_set_regen_blocks(h, 64) == 0
     with pytest.raises(CkksError) as ei:
