@@ -159,9 +159,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5], default=2,
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6], default=2,
                     help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
-                         "5: mixed 64-ciphertext stream")
+                         "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36")
     ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
                     help="which key variants to time (the headline is always the regenerated one when timed)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -292,10 +292,14 @@ def other_workload(args) -> int:
     from rns_ckks_key_amd.api import Context, chain_primes, to_device
 
     primes = chain_primes(LOG_N, BITS, L + K)
-    wl = synth.WORKLOADS[args.workload]
-    d = synth.draw(args.workload, primes)
     variants = [v for v in ("regen", "stored") if args.variant in ("both", v)]
-    res = {"metric": f"workload {args.workload}: {wl.name}", "unit": "key-switches/s", "n_gpus": 1,
+    if args.workload == 6:
+        name, unit = "multiply + relinearise (s^2 key) + rescale, N=2^16, batch 8 at level 36 -> 35", "products/s"
+    else:
+        wl = synth.WORKLOADS[args.workload]
+        d = synth.draw(args.workload, primes)
+        name, unit = wl.name, "key-switches/s"
+    res = {"metric": f"workload {args.workload}: {name}", "unit": unit, "n_gpus": 1,
            "dtype": "u32", "data": "synthetic", "steps": args.steps, "warmup": args.warmup}
     if args.workload == 3:
         ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
@@ -338,6 +342,39 @@ def other_workload(args) -> int:
             res[v] = {"key_switches_per_s": round(16 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
                       "hbm_roofline_frac": round(hbm_bytes(LEVEL, 1, v == "regen", 16) / (ms * 1e-3) / HBM_PEAK, 4),
                       "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+    elif args.workload == 6:
+        # batch 8 at level 36: x (x) y, relinearisation with the s^2 key, rescale to level 35
+        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+        rng = np.random.default_rng(6006)
+        xs = [to_device(np.stack([np.stack([synth.residues(rng, primes[:LEVEL], N) for _ in range(2)])
+                                  for _ in range(BATCH)])) for _ in range(2)]
+        kb = to_device(synth.uniform_key_rows(6000, primes, DNUM, N))
+        seed = rng.bytes(32)
+        ka = ctx.expand_a(seed)
+        out = torch.empty((BATCH, 2, LEVEL - 1, N), dtype=torch.int32, device="cuda")
+        for v in variants:
+            fn = lambda i, v=v: ctx.mul_relin_rescale(xs[0], xs[1], LEVEL, kb, key_seed=seed if v == "regen" else None,
+                                                       key_a=ka if v == "stored" else None, out=out)
+            ms = time_calls(fn, args.steps, args.warmup, torch)
+            ctx.profile(True)
+            for i in range(args.steps):
+                fn(i)
+            ctx.profile(False)
+            prof = ctx.profile_read()
+            res[v] = {"mul_relin_rescale_per_s": round(BATCH / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+        ms_r = time_calls(lambda i: ctx.rescale(xs[0], LEVEL, out=out), args.steps, args.warmup, torch)
+        ctx.profile(True)
+        for i in range(args.steps):
+            ctx.rescale(xs[0], LEVEL, out=out)
+        ctx.profile(False)
+        prof = ctx.profile_read()
+        res["rescale"] = {"ciphertexts_per_s": round(BATCH / (ms_r * 1e-3), 1), "ms_per_call": round(ms_r, 4),
+                          "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+        t_tensor = res[variants[0]]["kernel_ms"]["tensor"] * 1e-3
+        tensor_bytes = 7 * BATCH * LEVEL * N * 4  # reads x0 x1 y0 y1, writes d0 d1 d2
+        res["tensor_roofline"] = {"bound": "hbm", "achieved_gbs": round(tensor_bytes / t_tensor / 1e9, 1),
+                                  "peak_gbs": HBM_PEAK / 1e9, "frac": round(tensor_bytes / t_tensor / HBM_PEAK, 4)}
     else:
         ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
         kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
