@@ -198,7 +198,7 @@ typedef enum {
   CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
   CKKS_K_MODDOWN_FINAL = 7,/* end of the standalone ModDown */
   CKKS_K_TENSOR = 8,       /* tensor product of two ciphertexts */
-  CKKS_K_RESCALE_CONV = 9, /* column INTT of the dropped limb, its reduction and column NTT */
+  CKKS_K_RESCALE_CONV = 9, /* rescale column passes: INTT of the dropped limb; its reduction and NTT per q_i */
   CKKS_K_RESCALE_FINAL = 10,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
   CKKS_K_CLASSES = 11
 } ckks_kernel_class;

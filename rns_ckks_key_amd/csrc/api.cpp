@@ -773,9 +773,9 @@ ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t leve
 namespace {
 
 // Rescale of `items` polynomials [level][N] (NTT domain), consecutive at stride level*N,
-// into out [level-1][N] at stride (level-1)*N: INTT of limb level-1 (row pass, then
-// the column pass inside the conversion kernel, which reduces it modulo each
-// q_i < q_{level-1} and applies the column NTT), then the row NTT fused with
+// into out [level-1][N] at stride (level-1)*N: INTT of limb level-1 (row pass and
+// column pass), its coefficients reduced modulo each q_i and column-transformed
+// under q_i (one broadcast column pass), then the row NTT fused with
 // (c_i - .) * q_{level-1}^-1.  Uses ctx->rowtmp and ctx->conv.
 hipError_t run_rescale(ckks_ctx* c, const uint32_t* src, uint32_t level, uint32_t* out, uint32_t items,
                        hipStream_t s) {
@@ -794,29 +794,16 @@ hipError_t run_rescale(ckks_ctx* c, const uint32_t* src, uint32_t level, uint32_
     e = ckks::launch_row(c->d, r, false, items, s);
   }
   if (e != hipSuccess) return e;
-  ckks::ConvArgs a{};
-  a.src = c->rowtmp;
-  a.src_item = N;
-  a.src_y = 0;
-  a.dst = c->conv;
-  a.dst_item = (uint64_t)(level - 1) * N;
-  a.dst_y = 0;
-  a.src_prime0 = level - 1;
-  a.src_prime_step = 0;
-  a.ns_max = 1;
-  a.ns_limit = 1;
-  a.scale = c->d.ninv + (level - 1);  // the column INTT's N^-1; the source basis has one prime
-  a.scale_y = 0;
-  a.conv = c->d.r64;                  // z_i = x mod q_i (REDC2 leaves x * 2^64 * 2^-64)
-  a.conv_y = 0;
-  a.conv_s = 0;
-  a.conv_by_abs = 0;
-  a.n_targets = level - 1;
-  a.skip = 0;
-  a.level = level - 1;
-  {
+  {  // column INTT (with N^-1) of the dropped limb: rowtmp now holds its coefficients
+    ckks::ColArgs ca{c->rowtmp, N, level - 1, 1, nullptr, 0};
     ProfScope p(c, CKKS_K_RESCALE_CONV, s);
-    e = ckks::launch_conv(c->d, a, 1, items, s);
+    e = ckks::launch_col(c->d, ca, false, true, items, s);
+  }
+  if (e != hipSuccess) return e;
+  {  // those coefficients modulo each q_i, column NTT under q_i
+    ckks::ColArgs cb{c->conv, (uint64_t)(level - 1) * N, 0, level - 1, c->rowtmp, N};
+    ProfScope p(c, CKKS_K_RESCALE_CONV, s);
+    e = ckks::launch_col(c->d, cb, true, false, items, s);
   }
   if (e != hipSuccess) return e;
   ckks::RowArgs f{};

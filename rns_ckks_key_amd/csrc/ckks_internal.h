@@ -65,6 +65,10 @@ struct ColArgs {
   uint32_t* data;
   uint64_t item_stride;
   uint32_t prime0, n_limbs;
+  // forward pass only, when bsrc != nullptr: every limb starts from bsrc[item] (one
+  // polynomial of values < 2^32) reduced modulo its prime, instead of its own data
+  const uint32_t* bsrc;
+  uint64_t bsrc_item_stride;
 };
 
 // Fused column INTT + scale + fast base conversion + column NTT.
