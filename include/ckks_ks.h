@@ -182,6 +182,32 @@ ckks_status ckks_mul_relin_rescale(const ckks_ctx *ctx, const uint32_t *x, const
                                    const uint32_t *key_b, const uint8_t *key_seed, const uint32_t *key_a,
                                    uint32_t *out, uint32_t batch, void *stream);
 
+/* One rotation key of a linear transform: key_b and, if key_a is NULL, the seed of
+ * its a-half (as in ckks_keyswitch), with its Galois element. */
+typedef struct {
+  const uint32_t *key_b;   /* [dnum][L+K][N] */
+  const uint32_t *key_a;   /* stored a-half [dnum][L+K][N], or NULL */
+  uint8_t key_seed[32];    /* used when key_a is NULL */
+  uint32_t galois_elt;     /* odd, < 2N */
+} ckks_rot_key;
+
+/* Baby-step/giant-step linear transform with both hoists: out[2][level][N] =
+ * sum_{j<n2} Rot_j(ModDown(S_j)), S_j = sum_{k<n1} D[j][k] * R_k in the extended
+ * basis, where R_0 = P*ct and R_k (k >= 1) = (P*sigma_k(c0) + acc_b^k, acc_a^k) is
+ * baby key k's inner product with ct's digits (one ModUp serves every baby step;
+ * one ModDown per giant step), and Rot_0 is the identity, Rot_j (j >= 1) the full
+ * key-switch with giant key j.  diags: D[n2][n1][level+K][N], NTT domain over
+ * q_0..q_{level-1}, p_0..p_{K-1}.  baby: n1-1 keys (host array), giant: n2-1 keys
+ * (host array).  1 <= n1 <= 16, 1 <= n2 <= 8; out may alias ct.  The pages name
+ * bootstrapping, whose linear transforms these are, as the cost centre (Perseus
+ * summary on ai4snews, "Synopsis"); the two hoists are those of Bossuat et al.,
+ * Eurocrypt 2021.  Uses the context's workspace: needs max_batch large enough
+ * for 2*n2 ModDown items and the R and S buffers.
+ * Errors: EINVAL (NULL), ERANGE (level, n1, n2, Galois element, workspace). */
+ckks_status ckks_linear_transform_bsgs(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, uint32_t n1,
+                                       uint32_t n2, const ckks_rot_key *baby, const ckks_rot_key *giant,
+                                       const uint32_t *diags, uint32_t *out, void *stream);
+
 /* Test knob: number of ChaCha blocks generated per 1024-word tile before the
  * rare continuation path runs (default 68, at least 64).  64 sends every tile
  * with a rejected word through the continuation path. */
@@ -196,11 +222,13 @@ typedef enum {
   CKKS_K_MODDOWN_CONV = 4, /* fused column INTT + P->Q conversion + column NTT */
   CKKS_K_IP_FINAL = 5,     /* inner product over the ciphertext primes + end of ModDown */
   CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
-  CKKS_K_MODDOWN_FINAL = 7,/* end of the standalone ModDown */
+  CKKS_K_MODDOWN_FINAL = 7,/* end of a standalone ModDown: row NTT fused with (x - .) * P^-1 */
   CKKS_K_TENSOR = 8,       /* tensor product of two ciphertexts */
   CKKS_K_RESCALE_CONV = 9, /* rescale column passes: INTT of the dropped limb; its reduction and NTT per q_i */
   CKKS_K_RESCALE_FINAL = 10,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
-  CKKS_K_CLASSES = 11
+  CKKS_K_BABY = 11,        /* baby steps of a linear transform in the extended basis */
+  CKKS_K_DIAG = 12,        /* diagonal sums of a linear transform, and the sum of its giant steps */
+  CKKS_K_CLASSES = 13
 } ckks_kernel_class;
 
 /* Measurement aid: while enabled, every launch of this context is bracketed by

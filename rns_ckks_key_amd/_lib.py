@@ -41,6 +41,12 @@ PU32 = ctypes.POINTER(ctypes.c_uint32)
 PU64 = ctypes.POINTER(ctypes.c_uint64)
 PCTX = ctypes.c_void_p
 
+class RotKey(ctypes.Structure):
+    """ckks_rot_key of include/ckks_ks.h."""
+    _fields_ = [("key_b", ctypes.c_void_p), ("key_a", ctypes.c_void_p), ("key_seed", ctypes.c_uint8 * 32),
+                ("galois_elt", ctypes.c_uint32)]
+
+
 class KsItem(ctypes.Structure):
     """ckks_ks_item of include/ckks_ks.h."""
     _fields_ = [("ct", ctypes.c_void_p), ("out", ctypes.c_void_p), ("key_b", ctypes.c_void_p),
@@ -64,6 +70,8 @@ _SIGS = {
     "ckks_expand_a": (ctypes.c_int, [PCTX, ctypes.c_char_p, P, P]),
     "ckks_keyswitch_multi": (ctypes.c_int, [PCTX, U32, ctypes.POINTER(KsItem), P]),
     "ckks_rescale": (ctypes.c_int, [PCTX, P, U32, P, U32, P]),
+    "ckks_linear_transform_bsgs": (ctypes.c_int, [PCTX, P, U32, U32, U32, ctypes.POINTER(RotKey),
+                                                  ctypes.POINTER(RotKey), P, P, P]),
     "ckks_mul_relin_rescale": (ctypes.c_int, [PCTX, P, P, U32, P, ctypes.c_char_p, P, P, U32, P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
     "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
@@ -71,7 +79,7 @@ _SIGS = {
 }
 
 KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final",
-                  "tensor", "rescale_conv", "rescale_final"]
+                  "tensor", "rescale_conv", "rescale_final", "baby", "diag"]
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import KERNEL_CLASSES, PCTX, U32, U64, CkksError, KsItem, check, lib
+from ._lib import KERNEL_CLASSES, PCTX, U32, U64, CkksError, KsItem, RotKey, check, lib
 
 __all__ = ["Context", "CkksError", "chain_primes", "to_device", "to_numpy"]
 
@@ -214,6 +214,31 @@ class Context:
                                          _ptr(y, (b, 2, level, self.n), "y"), level, _ptr(key_b, kshape, "key_b"),
                                          _seed(key_seed), _ptr(key_a, kshape, "key_a"),
                                          _ptr(out, (b, 2, level - 1, self.n), "out"), b, _stream()))
+        return out
+
+    def _rot_keys(self, keys: list):
+        kshape = (self.dnum, self.L + self.K, self.n)
+        arr = (RotKey * max(1, len(keys)))()
+        for i, (key_b, galois, seed, key_a) in enumerate(keys):
+            arr[i].key_b = _ptr(key_b, kshape, "key_b")
+            arr[i].key_a = _ptr(key_a, kshape, "key_a") if key_a is not None else None
+            if key_a is None:
+                ctypes.memmove(arr[i].key_seed, _seed(seed), 32)
+            arr[i].galois_elt = galois
+        return arr
+
+    def linear_transform_bsgs(self, ct: torch.Tensor, level: int, diags: torch.Tensor, baby: list, giant: list,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+        """sum_j Rot_j(ModDown(sum_k D[j][k] * R_k)); baby/giant: lists of (key_b, galois, seed or None, key_a or None).
+
+        diags: [n2][n1][level+K][N]; len(baby) = n1 - 1, len(giant) = n2 - 1."""
+        n2, n1 = diags.shape[0], diags.shape[1]
+        if out is None:
+            out = torch.empty((2, level, self.n), dtype=torch.int32, device=ct.device)
+        check(lib.ckks_linear_transform_bsgs(self._h, _ptr(ct, (2, level, self.n), "ct"), level, n1, n2,
+                                             self._rot_keys(baby), self._rot_keys(giant),
+                                             _ptr(diags, (n2, n1, level + self.K, self.n), "diags"),
+                                             _ptr(out, (2, level, self.n), "out"), _stream()))
         return out
 
     def expand_a(self, seed: bytes, out: torch.Tensor | None = None, device="cuda") -> torch.Tensor:

@@ -123,7 +123,7 @@ struct Host {
   uint32_t log_n = 0, n = 0, L = 0, K = 0, dnum = 0, alpha = 0;
   std::vector<uint32_t> q, qinv, psi;
   std::vector<uint32_t> tw, itw;
-  std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one, r2, rs_inv;
+  std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one, r2, rs_inv, p_mod;
   std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound, r64tab;
 };
 
@@ -196,6 +196,7 @@ void build_tables(Host& h) {
   h.md_conv64.resize((size_t)K * L);
   h.md_fin_ks.resize(L);
   h.md_fin_pl.resize(L);
+  h.p_mod.resize(L);
   for (uint32_t k = 0; k < K; ++k) {
     const uint32_t pk = h.q[L + k];
     uint32_t ph = 1;
@@ -219,6 +220,7 @@ void build_tables(Host& h) {
     for (uint32_t k = 0; k < K; ++k) p = mulmod(p, h.q[L + k] % qi, qi);
     const uint32_t pinv = invmod(p, qi);
     h.md_fin_pl[i] = mont(pinv, qi);
+    h.p_mod[i] = mont(p, qi);
     h.md_fin_ks[i] = mont(mulmod(pinv, r32(qi), qi), qi);
   }
 }
@@ -296,6 +298,7 @@ ckks_status upload_tables(ckks_ctx* c) {
       {h.r2.data(), bytes_of(h.r2), (const void**)&d.r2},
       {h.r64tab.data(), bytes_of(h.r64tab), (const void**)&d.r64},
       {h.rs_inv.data(), bytes_of(h.rs_inv), (const void**)&d.rs_inv},
+      {h.p_mod.data(), bytes_of(h.p_mod), (const void**)&d.p_mod},
   };
   size_t total = 0;
   for (auto& p : parts) total += (p.bytes + 255) & ~size_t(255);
@@ -460,6 +463,91 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   if (e != hipSuccess) return e;
   ProfScope p(c, CKKS_K_IP_FINAL, s);
   return ckks::launch_ip(c->d, ip, true, level, s);
+}
+
+// ModUp of one ciphertext ct [2][level][N] into ctx->ext with the digits' NTT finished
+// (row half; own limbs copied from c1): the shared start of every hoisted call.
+hipError_t run_hoisted_digits(ckks_ctx* c, const uint32_t* ct, uint32_t level, hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 0, level, 1, s);
+  if (e != hipSuccess) return e;
+  for (uint32_t j = 0; j < digits_at(h, level); ++j) {
+    ckks::RowArgs r{};
+    r.src = c->ext + (uint64_t)j * (h.L + h.K) * N;
+    r.dst = c->ext + (uint64_t)j * (h.L + h.K) * N;
+    r.src_item_stride = r.dst_item_stride = 0;
+    r.prime0 = 0;
+    r.n_limbs = level + h.K;
+    r.own_lo = j * h.alpha;
+    r.own_n = std::min(h.alpha, level - j * h.alpha);
+    r.own_src = ct + (uint64_t)level * N;
+    r.own_item_stride = 0;
+    r.level = level;
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, true, 1, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ModDown of `items` extended polynomials x [level+K][N] (stride x_item) into out
+// [level][N] (stride out_item).  Uses ctx->rowtmp and ctx->conv.
+hipError_t run_moddown(ckks_ctx* c, const uint32_t* x, uint64_t x_item, uint32_t level, uint32_t* out,
+                       uint64_t out_item, uint32_t items, hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n;
+  ckks::RowArgs r{};
+  r.src = x + (uint64_t)level * N;
+  r.src_item_stride = x_item;
+  r.dst = c->rowtmp;
+  r.dst_item_stride = (uint64_t)h.K * N;
+  r.prime0 = h.L;
+  r.n_limbs = h.K;
+  hipError_t e;
+  {
+    ProfScope p(c, CKKS_K_ROW, s);
+    e = ckks::launch_row(c->d, r, false, items, s);
+  }
+  if (e != hipSuccess) return e;
+  ckks::ConvArgs a{};
+  a.src = c->rowtmp;
+  a.src_item = (uint64_t)h.K * N;
+  a.src_y = 0;
+  a.dst = c->conv;
+  a.dst_item = (uint64_t)level * N;
+  a.dst_y = 0;
+  a.src_prime0 = h.L;
+  a.src_prime_step = 0;
+  a.ns_max = h.K;
+  a.ns_limit = h.K;
+  a.scale = c->d.md_scale_pl;
+  a.scale_y = 0;
+  a.conv = c->d.md_conv64;
+  a.conv_y = 0;
+  a.conv_s = h.L;
+  a.conv_by_abs = 0;
+  a.n_targets = level;
+  a.skip = 0;
+  a.level = level;
+  {
+    ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
+    e = ckks::launch_conv(c->d, a, 1, items, s);
+  }
+  if (e != hipSuccess) return e;
+  // row NTT fused with (x_i - .) * P^-1
+  ckks::RowArgs f{};
+  f.src = c->conv;
+  f.src_item_stride = (uint64_t)level * N;
+  f.dst = out;
+  f.dst_item_stride = out_item;
+  f.prime0 = 0;
+  f.n_limbs = level;
+  f.cmb = x;
+  f.cmb_item_stride = x_item;
+  f.cmb_factor = c->d.md_fin_pl;
+  ProfScope p(c, CKKS_K_MODDOWN_FINAL, s);
+  return ckks::launch_row(c->d, f, true, items, s);
 }
 
 }  // namespace
@@ -685,62 +773,10 @@ ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, 
   if (st) return st;
   if (!x || !out) return fail(CKKS_EINVAL, "x or out is NULL");
   if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_device(c))) return st;
-  hipStream_t s = (hipStream_t)stream;
-  const Host& h = c->h;
-  const uint64_t N = h.n, El = level + h.K;
-  ckks::RowArgs r{};
-  r.src = x + (uint64_t)level * N;
-  r.src_item_stride = El * N;
-  r.dst = c->rowtmp;
-  r.dst_item_stride = (uint64_t)h.K * N;
-  r.prime0 = h.L;
-  r.n_limbs = h.K;
-  hipError_t e;
-  {
-    ProfScope p(c, CKKS_K_ROW, s);
-    e = ckks::launch_row(c->d, r, false, batch, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "ModDown row pass");
-  ckks::ConvArgs a{};
-  a.src = c->rowtmp;
-  a.src_item = (uint64_t)h.K * N;
-  a.src_y = 0;
-  a.dst = c->conv;
-  a.dst_item = (uint64_t)level * N;
-  a.dst_y = 0;
-  a.src_prime0 = h.L;
-  a.src_prime_step = 0;
-  a.ns_max = h.K;
-  a.ns_limit = h.K;
-  a.scale = c->d.md_scale_pl;
-  a.scale_y = 0;
-  a.conv = c->d.md_conv64;
-  a.conv_y = 0;
-  a.conv_s = h.L;
-  a.conv_by_abs = 0;
-  a.n_targets = level;
-  a.skip = 0;
-  a.level = level;
-  {
-    ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
-    e = ckks::launch_conv(c->d, a, 1, batch, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "ModDown conversion");
-  ckks::RowArgs r2{};
-  r2.src = c->conv;
-  r2.dst = c->conv;
-  r2.src_item_stride = r2.dst_item_stride = (uint64_t)level * N;
-  r2.prime0 = 0;
-  r2.n_limbs = level;
-  {
-    ProfScope p(c, CKKS_K_ROW, s);
-    e = ckks::launch_row(c->d, r2, true, batch, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "ModDown row NTT");
-  ProfScope p(c, CKKS_K_MODDOWN_FINAL, s);
-  return hip_status(ckks::launch_moddown_final(c->d, x, El * N, c->conv, (uint64_t)level * N, out,
-                                               (uint64_t)level * N, level, batch, s),
-                    "ModDown final");
+  const uint64_t N = c->h.n;
+  return hip_status(run_moddown(c, x, (uint64_t)(level + c->h.K) * N, level, out, (uint64_t)level * N, batch,
+                                (hipStream_t)stream),
+                    "ModDown");
 }
 
 ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
@@ -879,6 +915,91 @@ ckks_status ckks_mul_relin_rescale(const ckks_ctx* cc, const uint32_t* x, const 
   return hip_status(run_rescale(c, pair, level, out, 2 * batch, s), "rescale");
 }
 
+ckks_status ckks_linear_transform_bsgs(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, uint32_t n1,
+                                       uint32_t n2, const ckks_rot_key* baby, const ckks_rot_key* giant,
+                                       const uint32_t* diags, uint32_t* out, void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!ct || !diags || !out) return fail(CKKS_EINVAL, "ct, diags or out is NULL");
+  if ((st = check_level(c, level))) return st;
+  if (n1 < 1 || n1 > ckks::kMaxGroup) return fail(CKKS_ERANGE, "n1 %u outside 1..%u", n1, ckks::kMaxGroup);
+  if (n2 < 1 || n2 > ckks::kMaxGiant) return fail(CKKS_ERANGE, "n2 %u outside 1..%u", n2, ckks::kMaxGiant);
+  if ((n1 > 1 && !baby) || (n2 > 1 && !giant)) return fail(CKKS_EINVAL, "baby or giant key array is NULL");
+  for (uint32_t k = 0; k + 1 < n1 + n2 - 1; ++k) {
+    const ckks_rot_key& key = k + 1 < n1 ? baby[k] : giant[k + 1 - n1];
+    if (!key.key_b) return fail(CKKS_EINVAL, "key %u has no key_b", k);
+    if ((st = check_galois(c, key.galois_elt))) return st;
+  }
+  const Host& h = c->h;
+  const uint64_t N = h.n, El = level + h.K;
+  // workspace: R (baby steps) and S (diagonal sums) in ctx->tens, then the giant-step
+  // inputs over R, the giant-step outputs over S
+  const uint64_t r_words = (uint64_t)(n1 - 1) * 2 * El * N, s_words = (uint64_t)n2 * 2 * El * N,
+                 ct_words = (uint64_t)n2 * 2 * level * N;
+  const uint64_t B = c->max_batch ? c->max_batch : 4096;
+  if (std::max(r_words, ct_words) + s_words > B * 3 * h.L * N || 2 * n2 * h.K > B * std::max(std::max(h.L, h.K), 2u) ||
+      n2 > B)
+    return fail(CKKS_ERANGE, "a %u x %u transform needs a larger context (max_batch %u)", n1, n2, c->max_batch);
+  if ((st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* rbuf = c->tens;
+  uint32_t* sbuf = c->tens + std::max(r_words, ct_words);
+  uint32_t* ctbuf = c->tens;
+  hipError_t e;
+  if (n1 > 1) {
+    e = run_hoisted_digits(c, ct, level, s);
+    if (e != hipSuccess) return hip_status(e, "hoisted ModUp");
+    ckks::ExtArgs a{};
+    a.level = level;
+    a.nd = digits_at(h, level);
+    a.ext = c->ext;
+    a.c0 = ct;
+    a.out = rbuf;
+    a.regen_blocks = c->regen_blocks;
+    a.n_keys = n1 - 1;
+    for (uint32_t k = 0; k + 1 < n1; ++k) {
+      a.key[k] = ckks::KeyRef{};
+      a.key[k].b = baby[k].key_b;
+      a.key[k].a = baby[k].key_a;
+      if (!baby[k].key_a) seed_words(baby[k].key_seed, a.key[k].seed);
+      a.key[k].galois = baby[k].galois_elt;
+    }
+    ProfScope p(c, CKKS_K_BABY, s);
+    e = ckks::launch_rot_ext(c->d, a, s);
+    if (e != hipSuccess) return hip_status(e, "baby steps");
+  }
+  {
+    ckks::DiagArgs d{level, n1, n2, ct, rbuf, diags, sbuf};
+    ProfScope p(c, CKKS_K_DIAG, s);
+    e = ckks::launch_diag_acc(c->d, d, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "diagonal sums");
+  if (n2 == 1) return hip_status(run_moddown(c, sbuf, El * N, level, out, (uint64_t)level * N, 2, s), "ModDown");
+  e = run_moddown(c, sbuf, El * N, level, ctbuf, (uint64_t)level * N, 2 * n2, s);
+  if (e != hipSuccess) return hip_status(e, "ModDown");
+  ckks::SumArgs sum{};
+  sum.n_src = n2;
+  sum.words = 2ull * level * N;
+  sum.src[0] = ctbuf;
+  for (uint32_t j = 1; j < n2; ++j) {  // giant step j: key-switch of ModDown(S_j), output over S
+    const uint32_t* cj = ctbuf + (uint64_t)j * 2 * level * N;
+    uint32_t* rj = sbuf + (uint64_t)j * 2 * level * N;
+    e = run_modup(c, cj + (uint64_t)level * N, 2ull * level * N, level, 1, s);
+    if (e != hipSuccess) return hip_status(e, "giant-step ModUp");
+    ckks::KeyRef k{};
+    k.b = giant[j - 1].key_b;
+    k.a = giant[j - 1].key_a;
+    if (!k.a) seed_words(giant[j - 1].key_seed, k.seed);
+    k.galois = giant[j - 1].galois_elt;
+    e = run_ip_moddown(c, cj, 2ull * level * N, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, 1, &k, rj, false, s);
+    if (e != hipSuccess) return hip_status(e, "giant-step key-switch");
+    sum.src[j] = rj;
+  }
+  ProfScope p(c, CKKS_K_DIAG, s);
+  return hip_status(ckks::launch_sum(c->d, sum, out, level, s), "sum of giant steps");
+}
+
 ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, uint32_t n_keys,
                                    const uint32_t* const* key_b, const uint8_t* key_seeds,
                                    const uint32_t* const* key_a, const uint32_t* galois_elts, uint32_t* out,
@@ -897,28 +1018,8 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
   if ((st = check_device(c))) return st;
   hipStream_t s = (hipStream_t)stream;
   const uint64_t N = c->h.n;
-  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 0, level, 1, s);
-  if (e != hipSuccess) return hip_status(e, "ModUp");
-  // the digits are shared by every key: finish their NTT once (row half, own limbs copied from c1)
-  const Host& h = c->h;
-  for (uint32_t j = 0; j < digits_at(h, level); ++j) {
-    ckks::RowArgs r{};
-    r.src = c->ext + (uint64_t)j * (h.L + h.K) * N;
-    r.dst = c->ext + (uint64_t)j * (h.L + h.K) * N;
-    r.src_item_stride = r.dst_item_stride = 0;
-    r.prime0 = 0;
-    r.n_limbs = level + h.K;
-    r.own_lo = j * h.alpha;
-    r.own_n = std::min(h.alpha, level - j * h.alpha);
-    r.own_src = ct + (uint64_t)level * N;
-    r.own_item_stride = 0;
-    r.level = level;
-    {
-      ProfScope p(c, CKKS_K_ROW, s);
-      e = ckks::launch_row(c->d, r, true, 1, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "digit row pass");
-  }
+  hipError_t e = run_hoisted_digits(c, ct, level, s);
+  if (e != hipSuccess) return hip_status(e, "hoisted ModUp");
   const uint32_t chunk = std::min<uint32_t>(c->max_batch, ckks::kMaxGroup);
   for (uint32_t k0 = 0; k0 < n_keys; k0 += chunk) {
     const uint32_t nk = std::min(chunk, n_keys - k0);

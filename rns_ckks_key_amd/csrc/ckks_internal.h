@@ -34,6 +34,7 @@ struct DevTables {
   const uint2* r2;          // [L+K] multiplier 2^32 mod q (undoes a Montgomery product's 2^-32)
   const uint32_t* r64;      // [L+K] 2^64 mod q (plain): constant of a one-source reduction
   const uint2* rs_inv;      // [L+1][L] q_{l-1}^-1 mod q_i (rescale at level l)
+  const uint2* p_mod;       // [L] P mod q_i
 };
 
 // Row pass over limbs: blocks of 1024 coefficients, one wave per block.
@@ -124,12 +125,42 @@ hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t i
 hipError_t launch_col(const DevTables& T, const ColArgs& a, bool fwd, bool scale_ninv, uint32_t items, hipStream_t s);
 hipError_t launch_conv(const DevTables& T, const ConvArgs& a, uint32_t groups, uint32_t items, hipStream_t s);
 hipError_t launch_ip(const DevTables& T, const IpArgs& a, bool final_pass, uint32_t n_limbs, hipStream_t s);
+// Baby steps of a linear transform in the extended basis (NTT domain), one per key
+// group: R_k = (P*sigma_k(c0) + acc_b, acc_a) over limbs e < level + K (the c0 term
+// only on ciphertext primes), from fully transformed hoisted digits.
+struct ExtArgs {
+  uint32_t level, nd;
+  const uint32_t* ext;       // digits [dnum][L+K][N], row NTT done, own limbs included
+  const uint32_t* c0;        // [level][N]
+  uint32_t* out;             // R [key group][2][level+K][N]
+  uint32_t regen_blocks;
+  uint32_t n_keys;
+  KeyRef key[kMaxGroup];
+};
+
+// Diagonal sums S_j = sum_k D[j][k] * R_k over the extended basis, R_0 = P*ct.
+constexpr uint32_t kMaxGiant = 8;
+struct DiagArgs {
+  uint32_t level, n1, n2;
+  const uint32_t* ct;        // [2][level][N]
+  const uint32_t* r;         // R_1.. [n1-1][2][level+K][N]
+  const uint32_t* diags;     // [n2][n1][level+K][N]
+  uint32_t* s;               // [n2][2][level+K][N]
+};
+
+// out [2][level][N] = sum of n_src polynomials of the same shape.
+struct SumArgs {
+  uint32_t n_src;
+  uint64_t words;            // 2 * level * N
+  const uint32_t* src[kMaxGroup];
+};
+
+hipError_t launch_rot_ext(const DevTables& T, const ExtArgs& a, hipStream_t s);
+hipError_t launch_diag_acc(const DevTables& T, const DiagArgs& a, hipStream_t s);
+hipError_t launch_sum(const DevTables& T, const SumArgs& a, uint32_t* out, uint32_t level, hipStream_t s);
 hipError_t launch_tensor(const DevTables& T, const uint32_t* x, const uint32_t* y, uint32_t* pair, uint32_t* d1,
                          uint32_t level, uint32_t items, hipStream_t s);
 hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
                          hipStream_t s);
-hipError_t launch_moddown_final(const DevTables& T, const uint32_t* x, uint64_t x_item, const uint32_t* conv,
-                                uint64_t conv_item, uint32_t* out, uint64_t out_item, uint32_t level,
-                                uint32_t items, hipStream_t s);
 
 }  // namespace ckks

@@ -114,6 +114,23 @@ def test_host_context_validates_calls_before_any_launch():
     assert mrr(x=None) == EINVAL
     assert mrr(sd=None) == EINVAL
     assert mrr() == EINVAL and "host-only" in lib.ckks_last_error().decode()
+    keys = (_lib.RotKey * 2)()
+    keys[0].key_b = keys[1].key_b = 0x1000
+    keys[0].galois_elt, keys[1].galois_elt = 5, 25
+
+    def lt(n1=2, n2=2, baby=keys, giant=keys, diags=fake, level=4):
+        return lib.ckks_linear_transform_bsgs(h, fake, level, n1, n2, baby, giant, diags, far, None)
+
+    assert lt(n1=0) == ERANGE
+    assert lt(n1=17) == ERANGE
+    assert lt(n2=9) == ERANGE
+    assert lt(level=5) == ERANGE
+    assert lt(diags=None) == EINVAL
+    assert lt(baby=None) == EINVAL
+    keys[1].galois_elt = 4
+    assert lt(n1=3) == ERANGE  # baby key 1 has an even Galois element
+    keys[1].galois_elt = 25
+    assert lt() == EINVAL and "host-only" in lib.ckks_last_error().decode()
     assert lib.ckks_ctx_set_regen_blocks(h, 63) == ERANGE
     assert lib.ckks_ctx_set_regen_blocks(h, 64) == 0
     with pytest.raises(CkksError) as ei:
