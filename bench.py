@@ -159,9 +159,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6], default=2,
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7], default=2,
                     help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
-                         "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36")
+                         "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36; "
+                         "7: 4 x 4 baby-step/giant-step linear transform at level 36")
     ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
                     help="which key variants to time (the headline is always the regenerated one when timed)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,6 +296,9 @@ def other_workload(args) -> int:
     variants = [v for v in ("regen", "stored") if args.variant in ("both", v)]
     if args.workload == 6:
         name, unit = "multiply + relinearise (s^2 key) + rescale, N=2^16, batch 8 at level 36 -> 35", "products/s"
+    elif args.workload == 7:
+        name, unit = ("double-hoisted baby-step/giant-step linear transform, N=2^16, level 36, n1 = n2 = 4 "
+                      "(16 diagonals, 3 baby + 3 giant rotation keys g = 5^k)", "transforms/s")
     else:
         wl = synth.WORKLOADS[args.workload]
         d = synth.draw(args.workload, primes)
@@ -375,6 +379,37 @@ def other_workload(args) -> int:
         tensor_bytes = 7 * BATCH * LEVEL * N * 4  # reads x0 x1 y0 y1, writes d0 d1 d2
         res["tensor_roofline"] = {"bound": "hbm", "achieved_gbs": round(tensor_bytes / t_tensor / 1e9, 1),
                                   "peak_gbs": HBM_PEAK / 1e9, "frac": round(tensor_bytes / t_tensor / HBM_PEAK, 4)}
+    elif args.workload == 7:
+        n1 = n2 = 4
+        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+        rng = np.random.default_rng(7007)
+        ct = to_device(np.stack([synth.residues(rng, primes[:LEVEL], N) for _ in range(2)]))
+        ext = primes[:LEVEL] + primes[L:]
+        diags = to_device(np.stack([np.stack([synth.residues(rng, ext, N) for _ in range(n1)]) for _ in range(n2)]))
+        gs = [pow(5, k, 2 * N) for k in range(1, n1)] + [pow(5, n1 * j, 2 * N) for j in range(1, n2)]
+        kbs = [to_device(synth.uniform_key_rows(7000 + i, primes, DNUM, N)) for i in range(len(gs))]
+        seeds = [rng.bytes(32) for _ in gs]
+        kas = [ctx.expand_a(sd) for sd in seeds]
+        out = torch.empty((2, LEVEL, N), dtype=torch.int32, device="cuda")
+        for v in variants:
+            keys = [(kbs[i], gs[i], seeds[i] if v == "regen" else None, kas[i] if v == "stored" else None)
+                    for i in range(len(gs))]
+            fn = lambda i, keys=keys: ctx.linear_transform_bsgs(ct, LEVEL, diags, keys[:n1 - 1], keys[n1 - 1:], out=out)
+            ms = time_calls(fn, args.steps, args.warmup, torch)
+            ctx.profile(True)
+            for i in range(args.steps):
+                fn(i)
+            ctx.profile(False)
+            prof = ctx.profile_read()
+            res[v] = {"transforms_per_s": round(1 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                      "rotations_per_s": round((n1 * n2) / (ms * 1e-3), 1),
+                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
+        t_diag = res[variants[0]]["kernel_ms"]["diag"] * 1e-3
+        # the diagonal sums read the diagonals and the baby steps and write the sums: n1*n2 + 2*(n1-1) + 2*n2
+        # extended limbs; the giant-step sum (same timer class) reads n2 ciphertexts and writes one
+        diag_bytes = ((n1 * n2 + 2 * (n1 - 1) + 2 * n2) * (LEVEL + K) + (n2 + 1) * 2 * LEVEL) * N * 4
+        res["diag_roofline"] = {"bound": "hbm", "achieved_gbs": round(diag_bytes / t_diag / 1e9, 1),
+                                "peak_gbs": HBM_PEAK / 1e9, "frac": round(diag_bytes / t_diag / HBM_PEAK, 4)}
     else:
         ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
         kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]

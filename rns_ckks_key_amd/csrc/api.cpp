@@ -982,20 +982,25 @@ ckks_status ckks_linear_transform_bsgs(const ckks_ctx* cc, const uint32_t* ct, u
   sum.n_src = n2;
   sum.words = 2ull * level * N;
   sum.src[0] = ctbuf;
-  for (uint32_t j = 1; j < n2; ++j) {  // giant step j: key-switch of ModDown(S_j), output over S
-    const uint32_t* cj = ctbuf + (uint64_t)j * 2 * level * N;
-    uint32_t* rj = sbuf + (uint64_t)j * 2 * level * N;
-    e = run_modup(c, cj + (uint64_t)level * N, 2ull * level * N, level, 1, s);
-    if (e != hipSuccess) return hip_status(e, "giant-step ModUp");
-    ckks::KeyRef k{};
+  // giant steps 1..n2-1: key-switches of ModDown(S_j), each with its own key, in one
+  // ModUp batch and one group of key-using launches; outputs over S
+  ckks::KeyRef keys[ckks::kMaxGroup];
+  for (uint32_t j = 1; j < n2; ++j) {
+    ckks::KeyRef& k = keys[j - 1];
+    k = ckks::KeyRef{};
     k.b = giant[j - 1].key_b;
     k.a = giant[j - 1].key_a;
     if (!k.a) seed_words(giant[j - 1].key_seed, k.seed);
     k.galois = giant[j - 1].galois_elt;
-    e = run_ip_moddown(c, cj, 2ull * level * N, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, 1, &k, rj, false, s);
-    if (e != hipSuccess) return hip_status(e, "giant-step key-switch");
-    sum.src[j] = rj;
+    k.ct = ctbuf + (uint64_t)j * 2 * level * N;
+    k.out = sbuf + (uint64_t)j * 2 * level * N;
+    sum.src[j] = k.out;
   }
+  e = run_modup(c, ctbuf + 2ull * level * N + (uint64_t)level * N, 2ull * level * N, level, n2 - 1, s);
+  if (e != hipSuccess) return hip_status(e, "giant-step ModUp");
+  e = run_ip_moddown(c, nullptr, 0, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, n2 - 1, keys, nullptr, false, s,
+                     true);
+  if (e != hipSuccess) return hip_status(e, "giant-step key-switches");
   ProfScope p(c, CKKS_K_DIAG, s);
   return hip_status(ckks::launch_sum(c->d, sum, out, level, s), "sum of giant steps");
 }
