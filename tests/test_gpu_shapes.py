@@ -116,6 +116,28 @@ def test_repeatable_and_stream_ordered():
     assert np.array_equal(host(out), first)
 
 
+@pytest.mark.parametrize("shape,levels", [((14, 5, 3, 2, 32), (4,)), ((15, 8, 4, 2, 32), (8, 5, 4))])
+def test_keyswitch_batch4_conversion_remainders(shape, levels):
+    # batch 4 puts the conversions' last partial round of (target, column) tasks on
+    # 2 or 4 lanes per task: 4 targets per workgroup (ring 2^14, level 4; ring 2^15,
+    # level 4's ModDown) and 8 (ring 2^15, levels 8 and 5)
+    announce(f"keyswitch shape {shape} batch 4")
+    pr, ctx = setup(shape)
+    rng = np.random.default_rng(11 * shape[0])
+    g = 25
+    s = synth.ternary(rng, pr.n)
+    s_src = oks.rotation_source(s, g, pr)
+    errs = [synth.gaussian(rng, pr.n) for _ in range(pr.dnum)]
+    seed = rng.bytes(32)
+    kb, ka = oks.keygen(pr, s, s_src, errs, seed)
+    dkb = gpu(kb)
+    for level in levels:
+        ct = np.stack([np.stack([rand_limbs(rng, pr.primes[:level], pr.n) for _ in range(2)]) for _ in range(4)])
+        got = host(ctx.keyswitch(gpu(ct), level, dkb, g, key_seed=seed))
+        want = oks.keyswitch(pr, ct, level, kb, g, key_a=ka)
+        assert np.array_equal(got, want), (level, first_mismatch(got, want))
+
+
 @functools.lru_cache(maxsize=None)
 def setup_wide():
     shape = (12, 8, 2, 8, 30)  # dnum = 8, the largest digit count: eight key tiles per workgroup
