@@ -152,12 +152,21 @@ def cpu_baseline(primes, draw, budget_s: float) -> dict:
 
 # ---------------------------------------------------------------- main
 
+def make_context(primes, max_batch: int, args):
+    from rns_ckks_key_amd.api import Context
+    ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=max_batch)
+    ctx.set_conv_mfma(args.conv == "matrix")
+    return ctx
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--conv", choices=["vector", "matrix"], default="vector",
+                    help="base conversion on the vector unit or the matrix cores")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7], default=2,
                     help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
@@ -192,7 +201,7 @@ def main() -> int:
     if args.workload != 2:
         return other_workload(args)
     primes = chain_primes(LOG_N, BITS, L + K)
-    ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+    ctx = make_context(primes, BATCH, args)
     d = synth.draw(2, primes)
     seed = d.keys[0].seed
     cts = np.stack(d.cts)                                   # [8][2][36][N]
@@ -270,6 +279,7 @@ def main() -> int:
                             "shape": [BATCH * 2, LEVEL, N]},
     }
     out["config"]["variant"] = head_name
+    out["config"]["conversion"] = "matrix cores (int8 MFMA)" if args.conv == "matrix" else "vector unit"
     if "stored" in res and head_name != "stored":
         st = res["stored"]
         sp = st["prof"]
@@ -306,7 +316,7 @@ def other_workload(args) -> int:
     res = {"metric": f"workload {args.workload}: {name}", "unit": unit, "n_gpus": 1,
            "dtype": "u32", "data": "synthetic", "steps": args.steps, "warmup": args.warmup}
     if args.workload == 3:
-        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
+        ctx = make_context(primes, 16, args)
         kb = to_device(synth.uniform_key_rows(3003, primes, DNUM, N))
         seed = d.keys[0].seed
         ka = ctx.expand_a(seed)
@@ -328,7 +338,7 @@ def other_workload(args) -> int:
                                         "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
         res["levels"] = per
     elif args.workload == 4:
-        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
+        ctx = make_context(primes, 16, args)
         ct = to_device(d.cts[0])
         kbs = [to_device(synth.uniform_key_rows(4000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
         kas = [ctx.expand_a(kd.seed) for kd in d.keys]
@@ -348,7 +358,7 @@ def other_workload(args) -> int:
                       "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
     elif args.workload == 6:
         # batch 8 at level 36: x (x) y, relinearisation with the s^2 key, rescale to level 35
-        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+        ctx = make_context(primes, BATCH, args)
         rng = np.random.default_rng(6006)
         xs = [to_device(np.stack([np.stack([synth.residues(rng, primes[:LEVEL], N) for _ in range(2)])
                                   for _ in range(BATCH)])) for _ in range(2)]
@@ -381,7 +391,7 @@ def other_workload(args) -> int:
                                   "peak_gbs": HBM_PEAK / 1e9, "frac": round(tensor_bytes / t_tensor / HBM_PEAK, 4)}
     elif args.workload == 7:
         n1 = n2 = 4
-        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=BATCH)
+        ctx = make_context(primes, BATCH, args)
         rng = np.random.default_rng(7007)
         ct = to_device(np.stack([synth.residues(rng, primes[:LEVEL], N) for _ in range(2)]))
         ext = primes[:LEVEL] + primes[L:]
@@ -411,7 +421,7 @@ def other_workload(args) -> int:
         res["diag_roofline"] = {"bound": "hbm", "achieved_gbs": round(diag_bytes / t_diag / 1e9, 1),
                                 "peak_gbs": HBM_PEAK / 1e9, "frac": round(diag_bytes / t_diag / HBM_PEAK, 4)}
     else:
-        ctx = Context(LOG_N, L, K, DNUM, primes, max_batch=16)
+        ctx = make_context(primes, 16, args)
         kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
         kas = [ctx.expand_a(kd.seed) for kd in d.keys] if "stored" in variants else None
         cts = [to_device(c) for c in d.cts]

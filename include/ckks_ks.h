@@ -213,6 +213,18 @@ ckks_status ckks_linear_transform_bsgs(const ckks_ctx *ctx, const uint32_t *ct, 
  * with a rejected word through the continuation path. */
 ckks_status ckks_ctx_set_regen_blocks(ckks_ctx *ctx, uint32_t blocks);
 
+/* Base conversion on the matrix cores.  on = 1: ModUp and ModDown conversions
+ * (every call that uses them) run the fused conversion kernel whose sums over
+ * sources are exact int8 matrix products (v_mfma_i32_32x32x32_i8 on 7-bit digits of
+ * the scaled source values and of the conversion constants), recombined and reduced
+ * on the vector unit; on = 0 (the default): the vector-unit kernel.  Both give
+ * bit-identical results (the conversion of Han and Ki, 2020, is exact integer
+ * arithmetic either way).  Available for N = 2^16 with 9..12 primes per digit and
+ * in the special part; the operand tables are built at context creation.
+ * Calls already enqueued are not affected.
+ * Errors: EINVAL (NULL ctx, host-only context), EUNSUPPORTED (on = 1 for another shape). */
+ckks_status ckks_ctx_set_conv_mfma(ckks_ctx *ctx, uint32_t on);
+
 /* Kernel classes of the per-kernel event timer. */
 typedef enum {
   CKKS_K_ROW = 0,          /* row pass of an NTT/INTT (1024-coefficient blocks) */

@@ -74,6 +74,7 @@ _SIGS = {
                                                   ctypes.POINTER(RotKey), P, P, P]),
     "ckks_mul_relin_rescale": (ctypes.c_int, [PCTX, P, P, U32, P, ctypes.c_char_p, P, P, U32, P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
+    "ckks_ctx_set_conv_mfma": (ctypes.c_int, [PCTX, U32]),
     "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
     "ckks_profile_read": (ctypes.c_int, [PCTX, ctypes.POINTER(ctypes.c_double), PU32, U32]),
 }

@@ -103,6 +103,10 @@ class Context:
     def set_regen_blocks(self, blocks: int) -> None:
         check(lib.ckks_ctx_set_regen_blocks(self._h, blocks))
 
+    def set_conv_mfma(self, on: bool) -> None:
+        """Base conversions on the matrix cores (True) or the vector unit (False)."""
+        check(lib.ckks_ctx_set_conv_mfma(self._h, 1 if on else 0))
+
     def profile(self, enable: bool) -> None:
         """Bracket every launch with HIP events on its stream (measurement aid)."""
         check(lib.ckks_profile_enable(self._h, 1 if enable else 0))

@@ -125,7 +125,80 @@ struct Host {
   std::vector<uint32_t> tw, itw;
   std::vector<uint2> ninv, mu_scale, md_scale_ks, md_scale_pl, md_fin_ks, md_fin_pl, one, r2, rs_inv, p_mod;
   std::vector<uint32_t> mu_conv, md_conv, md_conv64, bound, r64tab;
+  // matrix-core conversion operands (ring 2^16 with 9..12 sources per conversion)
+  bool mx_ok = false;
+  std::vector<uint32_t> mx_w;                     // [L+K][12]
+  std::vector<uint8_t> mx_up, mx_md_ks, mx_md_pl; // tiles of 2048 bytes
 };
+
+// One matrix-core operand tile (two K steps x 64 lanes x 16 bytes) for the target
+// pair (2mt, 2mt+1) of a conversion.  Lane l holds row m = l & 31, i.e. pair member
+// p = (m >> 2) & 1 and digit position e = 4(m >> 3) + (m & 3), and K half h = l >> 5.
+// Byte i of K step kappa is g = 16 kappa + i: source s = 6h + g/5, source digit
+// a = g % 5 (g < 30).  Its value is 7-bit digit e - a of the constant cst(p, s) when
+// 0 <= e - a <= 4, else 0 (cst returns 0 for a missing target).
+template <class F>
+void mx_tile(uint8_t* out, uint32_t ns, F cst) {
+  for (uint32_t kap = 0; kap < 2; ++kap)
+    for (uint32_t l = 0; l < 64; ++l) {
+      const uint32_t m = l & 31, h = l >> 5, p = (m >> 2) & 1, e = 4 * (m >> 3) + (m & 3);
+      for (uint32_t i = 0; i < 16; ++i) {
+        const uint32_t g = 16 * kap + i;
+        uint8_t b = 0;
+        if (g < 30) {
+          const uint32_t src = 6 * h + g / 5, a = g % 5;
+          if (src < ns && e >= a && e - a <= 4) b = (uint8_t)((cst(p, src) >> (7 * (e - a))) & 127u);
+        }
+        out[(kap * 64 + l) * 16 + i] = b;
+      }
+    }
+}
+
+// Operand tables of the matrix-core conversion.  The vector path multiplies by
+// constants c' carrying 2^64 and reduces by 2^-64; the effective constant is
+// c' * 2^-64 mod q, whose digits go into the tiles, so both paths give the same residue.
+void build_mx_tables(Host& h) {
+  const uint32_t L = h.L, K = h.K, E = L + K, A = h.alpha, D = h.dnum, T = ckks::kMxTiles;
+  h.mx_ok = h.log_n == 16 && A >= 9 && A <= 12 && K >= 9 && K <= 12 && E <= 2 * T;
+  if (!h.mx_ok) return;
+  std::vector<uint32_t> inv64(E);
+  for (uint32_t t = 0; t < E; ++t) inv64[t] = invmod(r64(h.q[t]), h.q[t]);
+  h.mx_w.assign((size_t)E * 12, 0);
+  for (uint32_t t = 0; t < E; ++t)
+    for (uint32_t e = 0; e < 9; ++e) h.mx_w[(size_t)t * 12 + e] = mulmod(powmod(2, 7 * e, h.q[t]), r32(h.q[t]), h.q[t]);
+  const size_t tile = 2048;
+  h.mx_up.assign((size_t)(L + 1) * D * T * tile, 0);
+  for (uint32_t l = 1; l <= L; ++l) {
+    const uint32_t d = (l + A - 1) / A;
+    for (uint32_t j = 0; j < d; ++j) {
+      const uint32_t lo = j * A, ns = std::min(lo + A, l) - lo, nt = l + K - ns;
+      for (uint32_t mt = 0; 2 * mt < nt; ++mt) {
+        auto cst = [&](uint32_t p, uint32_t src) -> uint32_t {
+          const uint32_t e = 2 * mt + p;
+          if (e >= nt) return 0;
+          const uint32_t dl = e < lo ? e : e + ns, tp = dl < l ? dl : L + (dl - l);
+          const uint32_t c = h.mu_conv[(((size_t)l * D + j) * A + src) * E + tp];
+          return mulmod(c, inv64[tp], h.q[tp]);
+        };
+        mx_tile(&h.mx_up[(((size_t)l * D + j) * T + mt) * tile], ns, cst);
+      }
+    }
+  }
+  h.mx_md_ks.assign((size_t)T * tile, 0);
+  h.mx_md_pl.assign((size_t)T * tile, 0);
+  for (uint32_t mt = 0; 2 * mt < L; ++mt) {
+    auto ks = [&](uint32_t p, uint32_t src) -> uint32_t {
+      const uint32_t e = 2 * mt + p;
+      return e < L ? mulmod(h.md_conv[(size_t)src * L + e], inv64[e], h.q[e]) : 0u;
+    };
+    auto pl = [&](uint32_t p, uint32_t src) -> uint32_t {
+      const uint32_t e = 2 * mt + p;
+      return e < L ? mulmod(h.md_conv64[(size_t)src * L + e], inv64[e], h.q[e]) : 0u;
+    };
+    mx_tile(&h.mx_md_ks[(size_t)mt * tile], K, ks);
+    mx_tile(&h.mx_md_pl[(size_t)mt * tile], K, pl);
+  }
+}
 
 void build_tables(Host& h) {
   const uint32_t n = h.n, E = h.L + h.K, L = h.L, K = h.K, A = h.alpha;
@@ -223,6 +296,7 @@ void build_tables(Host& h) {
     h.p_mod[i] = mont(p, qi);
     h.md_fin_ks[i] = mont(mulmod(pinv, r32(qi), qi), qi);
   }
+  build_mx_tables(h);
 }
 
 }  // namespace
@@ -234,6 +308,11 @@ struct ckks_ctx {
   uint32_t max_batch = 0;
   int device = -1;
   uint32_t regen_blocks = ckks::kDefaultRegenBlocks;
+  // matrix-core conversion: operand tables on the device, and whether calls use them
+  const uint4* mx_up = nullptr;
+  const uint4* mx_md_ks = nullptr;
+  const uint4* mx_md_pl = nullptr;
+  bool conv_mfma = false;
   // workspace (items = max_batch)
   void* ws = nullptr;
   uint64_t ws_bytes = 0;
@@ -300,6 +379,12 @@ ckks_status upload_tables(ckks_ctx* c) {
       {h.rs_inv.data(), bytes_of(h.rs_inv), (const void**)&d.rs_inv},
       {h.p_mod.data(), bytes_of(h.p_mod), (const void**)&d.p_mod},
   };
+  if (h.mx_ok) {
+    parts.push_back({h.mx_w.data(), bytes_of(h.mx_w), (const void**)&d.mx_w});
+    parts.push_back({h.mx_up.data(), bytes_of(h.mx_up), (const void**)&c->mx_up});
+    parts.push_back({h.mx_md_ks.data(), bytes_of(h.mx_md_ks), (const void**)&c->mx_md_ks});
+    parts.push_back({h.mx_md_pl.data(), bytes_of(h.mx_md_pl), (const void**)&c->mx_md_pl});
+  }
   size_t total = 0;
   for (auto& p : parts) total += (p.bytes + 255) & ~size_t(255);
   if (hipMalloc(&c->dev_tables, total) != hipSuccess)
@@ -400,6 +485,10 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
   a.skip = 1;
   a.level = level;
   a.n_targets = 0;  // per digit: level + K - (digit size), computed in the kernel
+  if (c->conv_mfma) {
+    a.mx = c->mx_up + (size_t)level * h.dnum * ckks::kMxTiles * 128;
+    a.mx_y = ckks::kMxTiles * 128;
+  }
   ProfScope p(c, CKKS_K_MODUP_CONV, s);
   return ckks::launch_conv(c->d, a, digits_at(h, level), items, s);
   return hipSuccess;
@@ -456,6 +545,7 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   a.n_targets = level;
   a.skip = 0;
   a.level = level;
+  if (c->conv_mfma) a.mx = c->mx_md_ks;
   {
     ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
     e = ckks::launch_conv(c->d, a, 2, n_ct * n_keys, s);
@@ -530,6 +620,7 @@ hipError_t run_moddown(ckks_ctx* c, const uint32_t* x, uint64_t x_item, uint32_t
   a.n_targets = level;
   a.skip = 0;
   a.level = level;
+  if (c->conv_mfma) a.mx = c->mx_md_pl;
   {
     ProfScope p(c, CKKS_K_MODDOWN_CONV, s);
     e = ckks::launch_conv(c->d, a, 1, items, s);
@@ -669,6 +760,15 @@ ckks_status ckks_ctx_set_regen_blocks(ckks_ctx* c, uint32_t blocks) {
   if (blocks < ckks::kRow / 16 || blocks > ckks::kMaxRegenBlocks)
     return fail(CKKS_ERANGE, "regen blocks %u outside %u..%u", blocks, ckks::kRow / 16, ckks::kMaxRegenBlocks);
   c->regen_blocks = blocks;
+  return ok();
+}
+
+ckks_status ckks_ctx_set_conv_mfma(ckks_ctx* c, uint32_t on) {
+  if (!c) return fail(CKKS_EINVAL, "ctx is NULL");
+  if (on && !c->h.mx_ok)
+    return fail(CKKS_EUNSUPPORTED, "matrix-core conversion needs N = 2^16 and 9..12 primes per digit and special part");
+  if (on && c->max_batch == 0) return fail(CKKS_EINVAL, "host-only context (max_batch = 0) has no device tables");
+  c->conv_mfma = on != 0;
   return ok();
 }
 

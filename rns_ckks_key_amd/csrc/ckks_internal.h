@@ -35,6 +35,7 @@ struct DevTables {
   const uint32_t* r64;      // [L+K] 2^64 mod q (plain): constant of a one-source reduction
   const uint2* rs_inv;      // [L+1][L] q_{l-1}^-1 mod q_i (rescale at level l)
   const uint2* p_mod;       // [L] P mod q_i
+  const uint4* mx_w;        // [L+K][3] 2^(7e+32) mod q, e = 0..8 (then zeros): matrix-core conversion
 };
 
 // Row pass over limbs: blocks of 1024 coefficients, one wave per block.
@@ -89,7 +90,14 @@ struct ConvArgs {
   uint32_t skip;             // 1: skip the source limbs' own range in the destination limbs
   uint32_t level;            // ext mapping: dlimb < level ? dlimb : L + dlimb - level (level=0: dlimb)
   uint32_t tchunks;          // targets split over this many workgroups (set by the launcher)
+  // Matrix-core conversion (ring 2^16, 9..12 sources): int8 A operands of target pair
+  // tiles, [group y][tile][K step][lane] uint4 from mx + y*mx_y; nullptr = vector path.
+  const uint4* mx;
+  uint32_t mx_y;
 };
+
+// Target-pair tiles per conversion group in the matrix-core operand tables.
+constexpr uint32_t kMxTiles = 32;
 
 struct KeyRef {
   const uint32_t* b;         // [dnum][L+K][N]

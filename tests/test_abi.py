@@ -137,3 +137,19 @@ def test_host_context_validates_calls_before_any_launch():
         _lib.check(ks(level=9))
     assert ei.value.name == "CKKS_ERANGE"
     ctx.close()
+
+
+def test_conv_mfma_switch_validates_the_shape():
+    # the matrix-core conversion exists for N = 2^16 with 9..12 primes per digit and special part
+    tiny = Context.for_chain(12, 4, 2, 2, 30, max_batch=0)
+    assert lib.ckks_ctx_set_conv_mfma(tiny.handle, 1) == EUNSUPPORTED
+    assert lib.ckks_ctx_set_conv_mfma(tiny.handle, 0) == 0
+    tiny.close()
+    boot = Context.for_chain(16, 36, 12, 3, 32, max_batch=0)
+    assert lib.ckks_ctx_set_conv_mfma(boot.handle, 1) == EINVAL  # host-only: no device tables
+    assert "host-only" in lib.ckks_last_error().decode()
+    boot.close()
+    wide = Context.for_chain(16, 36, 6, 6, 32, max_batch=0)  # six primes per digit
+    assert lib.ckks_ctx_set_conv_mfma(wide.handle, 1) == EUNSUPPORTED
+    wide.close()
+    assert lib.ckks_ctx_set_conv_mfma(None, 1) == EINVAL
