@@ -385,10 +385,6 @@ def other_workload(args) -> int:
         prof = ctx.profile_read()
         res["rescale"] = {"ciphertexts_per_s": round(BATCH / (ms_r * 1e-3), 1), "ms_per_call": round(ms_r, 4),
                           "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-        t_tensor = res[variants[0]]["kernel_ms"]["tensor"] * 1e-3
-        tensor_bytes = 7 * BATCH * LEVEL * N * 4  # reads x0 x1 y0 y1, writes d0 d1 d2
-        res["tensor_roofline"] = {"bound": "hbm", "achieved_gbs": round(tensor_bytes / t_tensor / 1e9, 1),
-                                  "peak_gbs": HBM_PEAK / 1e9, "frac": round(tensor_bytes / t_tensor / HBM_PEAK, 4)}
     elif args.workload == 7:
         n1 = n2 = 4
         ctx = make_context(primes, BATCH, args)

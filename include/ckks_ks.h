@@ -175,8 +175,10 @@ ckks_status ckks_rescale(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level
  * (key_b, and key_a or key_seed as in ckks_keyswitch) switches from s^2 to s.
  * x, y: [batch][2][level][N]; level >= 2.  Relinearisation is one of the
  * key-switches whose key the pages regenerate in-kernel (Perseus summary on
- * ai4snews, "Interpretation" paragraph 2).  Uses the context's workspace (the
- * tensor product needs 3*batch*level*N words of it).
+ * ai4snews, "Interpretation" paragraph 2).  The tensor product is never stored:
+ * ModUp's inverse row pass forms d2, the final inner-product pass forms d0, d1 and
+ * the own-digit limbs of d2 from x and y.  Uses the context's workspace (the
+ * relinearised pair takes 2*batch*level*N words of it).  out may alias x or y.
  * Errors: EINVAL (NULL, no key_a or seed), ERANGE (level outside 2..L, batch). */
 ckks_status ckks_mul_relin_rescale(const ckks_ctx *ctx, const uint32_t *x, const uint32_t *y, uint32_t level,
                                    const uint32_t *key_b, const uint8_t *key_seed, const uint32_t *key_a,
@@ -235,7 +237,7 @@ typedef enum {
   CKKS_K_IP_FINAL = 5,     /* inner product over the ciphertext primes + end of ModDown */
   CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
   CKKS_K_MODDOWN_FINAL = 7,/* end of a standalone ModDown: row NTT fused with (x - .) * P^-1 */
-  CKKS_K_TENSOR = 8,       /* tensor product of two ciphertexts */
+  CKKS_K_TENSOR = 8,       /* reserved: the tensor product is formed inside the relinearisation's kernels */
   CKKS_K_RESCALE_CONV = 9, /* rescale column passes: INTT of the dropped limb; its reduction and NTT per q_i */
   CKKS_K_RESCALE_FINAL = 10,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
   CKKS_K_BABY = 11,        /* baby steps of a linear transform in the extended basis */

@@ -442,8 +442,9 @@ void seed_words(const uint8_t* seed, uint32_t out[8]) {
 uint32_t digits_at(const Host& h, uint32_t level) { return (level + h.alpha - 1) / h.alpha; }
 
 // Steps 1-2: INTT row half of c1 and the fused ModUp conversion into ctx->ext.
+// c1b (optional): c1 is the elementwise product c1 * c1b, formed in the row pass.
 hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, uint32_t level, uint32_t items,
-                     hipStream_t s, const uint32_t* const* c1_items = nullptr) {
+                     hipStream_t s, const uint32_t* const* c1_items = nullptr, const uint32_t* c1b = nullptr) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::RowArgs r{};
@@ -453,6 +454,7 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
     for (uint32_t i = 0; i < items; ++i) r.srcs[i] = c1_items[i];
   }
   r.dst = c->rowtmp;
+  r.src2 = c1b;
   r.src_item_stride = c1_item_stride;
   r.dst_item_stride = (uint64_t)level * N;
   r.prime0 = 0;
@@ -498,7 +500,7 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
 hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
                           uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
                           bool digits_ntt, hipStream_t s, bool per_group = false,
-                          const uint32_t* add_a = nullptr, uint64_t add_a_item = 0) {
+                          const uint32_t* ty = nullptr) {
   const Host& h = c->h;
   const uint64_t N = h.n;
   ckks::IpArgs ip{};
@@ -517,8 +519,7 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   ip.per_group = per_group ? 1u : 0u;
   ip.n_keys = n_keys;
   for (uint32_t k = 0; k < n_keys; ++k) ip.key[k] = keys[k];
-  ip.add_a = add_a;
-  ip.add_a_item = add_a_item;
+  ip.ty = ty;
   hipError_t e;
   {
     ProfScope p(c, CKKS_K_IP_SPECIAL, s);
@@ -992,25 +993,18 @@ ckks_status ckks_mul_relin_rescale(const ckks_ctx* cc, const uint32_t* x, const 
   if ((st = check_device(c))) return st;
   hipStream_t s = (hipStream_t)stream;
   const uint64_t N = c->h.n, ln = (uint64_t)level * N;
-  uint32_t* pair = c->tens;                   // [B][2][l][N]: (d0, d2), later the relinearised (e0, e1)
-  uint32_t* d1 = c->tens + (uint64_t)batch * 2 * ln;  // [B][l][N]
-  hipError_t e;
-  {
-    ProfScope p(c, CKKS_K_TENSOR, s);
-    e = ckks::launch_tensor(c->d, x, y, pair, d1, level, batch, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "tensor product");
-  e = run_modup(c, pair + ln, 2 * ln, level, batch, s);
+  uint32_t* pair = c->tens;  // [B][2][l][N]: the relinearised (e0, e1)
+  // The tensor product (d0, d1, d2) = (x0 y0, x0 y1 + x1 y0, x1 y1) is never stored:
+  // ModUp's row pass forms d2, the final inner-product pass forms d0, d1 and d2's own limbs.
+  hipError_t e = run_modup(c, x + ln, 2 * ln, level, batch, s, nullptr, y + ln);
   if (e != hipSuccess) return hip_status(e, "ModUp");
   ckks::KeyRef k{};
   k.b = key_b;
   k.a = key_a;
   if (!key_a) seed_words(key_seed, k.seed);
   k.galois = 1;
-  // With Galois element 1 every final-pass workgroup reads c0, c1 and d1 only at the
-  // (limb, block) it writes, so the relinearised pair may overwrite (d0, d2) in place.
-  e = run_ip_moddown(c, pair, 2 * ln, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k, pair, false,
-                     s, false, d1, ln);
+  e = run_ip_moddown(c, x, 2 * ln, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k, pair, false,
+                     s, false, y);
   if (e != hipSuccess) return hip_status(e, "relinearisation");
   return hip_status(run_rescale(c, pair, level, out, 2 * batch, s), "rescale");
 }

@@ -59,6 +59,9 @@ struct RowArgs {
   // forward pass only, when cmb != nullptr: dst = (cmb - NTT(src)) * cmb_factor[y]
   const uint32_t* cmb;
   uint64_t cmb_item_stride;
+  // inverse pass only, when src2 != nullptr: the source limb is src * src2 (elementwise,
+  // same layout and item stride as src), the x1 y1 part of a tensor product
+  const uint32_t* src2;
   const uint2* cmb_factor;
 };
 
@@ -125,8 +128,9 @@ struct IpArgs {
                              //    digits at ext + g * ext_ct_stride (n_ct = 1)
   uint32_t n_keys;
   KeyRef key[kMaxGroup];     // per key group (grid z)
-  const uint32_t* add_a;     // optional [item][level][N] added to the final a-half output
-  uint64_t add_a_item;
+  // Relinearisation: the ciphertext is the tensor product of ct (x) and ty (y), both
+  // [ct][2][level][N] with stride ct_ct_stride, formed in the final pass (Galois element 1).
+  const uint32_t* ty;
 };
 
 hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t items, hipStream_t s);
@@ -166,8 +170,6 @@ struct SumArgs {
 hipError_t launch_rot_ext(const DevTables& T, const ExtArgs& a, hipStream_t s);
 hipError_t launch_diag_acc(const DevTables& T, const DiagArgs& a, hipStream_t s);
 hipError_t launch_sum(const DevTables& T, const SumArgs& a, uint32_t* out, uint32_t level, hipStream_t s);
-hipError_t launch_tensor(const DevTables& T, const uint32_t* x, const uint32_t* y, uint32_t* pair, uint32_t* d1,
-                         uint32_t level, uint32_t items, hipStream_t s);
 hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
                          hipStream_t s);
 
