@@ -397,6 +397,10 @@ ckks_status upload_tables(ckks_ctx* c) {
     *p.dst = dst;
     off += (p.bytes + 255) & ~size_t(255);
   }
+  // the matrix-core operand tiles are only read on the device
+  std::vector<uint8_t>().swap(h.mx_up);
+  std::vector<uint8_t>().swap(h.mx_md_ks);
+  std::vector<uint8_t>().swap(h.mx_md_pl);
   return CKKS_OK;
 }
 
