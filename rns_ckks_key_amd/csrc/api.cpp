@@ -320,7 +320,7 @@ struct ckks_ctx {
   uint32_t* ext = nullptr;     // [B][dnum][L+K][N]
   uint32_t* tmpP = nullptr;    // [B][2][K][N]
   uint32_t* conv = nullptr;    // [B][2][L][N]
-  uint32_t* tens = nullptr;    // [B][3][L][N]: tensor product (d0, d2 pair, then d1)
+  uint32_t* tens = nullptr;    // [B][3][L][N]: relinearised pair of a multiply; R and S buffers of a transform
   // per-launch event timer (measurement aid)
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev;     // pool: 2 events per record
