@@ -134,6 +134,56 @@ def test_hoisted_tiny_equals_oracle():
     assert np.array_equal(got, want), first_mismatch(got, want)
 
 
+def test_hoisted_tiny_forty_keys_and_the_key_limit():
+    # 40 keys cross the launch groups of 16 key groups (16 + 16 + 8); 64 is the limit
+    announce("hoisted tiny 40 keys")
+    pr = params("tiny")
+    ctx = context("tiny", 2)
+    rng = np.random.default_rng(40)
+    s = synth.ternary(rng, pr.n)
+    twon = 2 * pr.n
+    gs = [pow(5, k, twon) if k % 7 else pow(5, k, twon) * (twon - 1) % twon for k in range(1, 41)]
+    keys, dk = [], []
+    for i, g in enumerate(gs):
+        errs = [synth.gaussian(rng, pr.n) for _ in range(pr.dnum)]
+        seed = rng.bytes(32)
+        kb, ka = oks.keygen(pr, s, oks.rotation_source(s, g, pr), errs, seed)
+        keys.append((kb, ka, g))
+        dk.append((gpu(kb), g, seed, gpu(ka) if i % 3 == 0 else None))
+    ct = _ct(rng, pr, 3, 1)[0]
+    got = host(ctx.keyswitch_hoisted(gpu(ct), 3, dk))
+    want = oks.keyswitch_hoisted(pr, ct, 3, keys)
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    from rns_ckks_key_amd.api import CkksError
+    with pytest.raises(CkksError) as ei:
+        ctx.keyswitch_hoisted(gpu(ct), 3, dk + dk[:25])  # 65 keys
+    assert ei.value.name == "CKKS_ERANGE"
+
+
+def test_multi_tiny_chunks_of_sixteen_against_oracle():
+    # 21 items at level 3 (one ModUp batch of 16, then 5) and 3 at level 2, five keys,
+    # stored and regenerated mixed: every output against the oracle
+    announce("multi tiny 24 items")
+    pr = params("tiny")
+    ctx = context("tiny", 16)
+    rng = np.random.default_rng(24)
+    keys = [oracle_key("tiny", g, 7) for g in (5, 25, 1, 8191, 125)]
+    gals = (5, 25, 1, 8191, 125)
+    items, want = [], []
+    for i in range(24):
+        k = i % 5
+        kb, ka, seed = keys[k][0], keys[k][1], keys[k][2]
+        level = 3 if i < 21 else 2
+        ct = _ct(rng, pr, level, 1)[0]
+        stored = i % 4 == 0
+        items.append((gpu(ct), level, gpu(kb), gals[k], None if stored else seed, gpu(ka) if stored else None, None))
+        want.append(oks.keyswitch(pr, ct, level, kb, gals[k], key_a=ka))
+    outs = ctx.keyswitch_multi(items)
+    for i, (o, w) in enumerate(zip(outs, want)):
+        got = host(o)
+        assert np.array_equal(got, w), (i, first_mismatch(got, w))
+
+
 @pytest.mark.parametrize("variant", ["regen", "stored"])
 def test_keyswitch_boot_batch8_sampled(variant):
     # the single key-switch workload: batch 8 at level 36, g = 5; ciphertexts 0 and 7 against the oracle
