@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 LOG_N, L, K, DNUM, BITS = 16, 36, 12, 3, 32
 N = 1 << LOG_N
 BATCH, LEVEL, GALOIS = 8, 36, 5
+SMALL_RING = (15, 20, 7, 3)           # log N, ciphertext primes, special primes, dnum of the smaller-ring workload
 ROTATE = 4
 
 # ---------------------------------------------------------------- work model
@@ -168,10 +169,11 @@ def main() -> int:
     ap.add_argument("--conv", choices=["vector", "matrix"], default="vector",
                     help="base conversion on the vector unit or the matrix cores")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7], default=2,
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7, 8], default=2,
                     help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
                          "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36; "
-                         "7: 4 x 4 baby-step/giant-step linear transform at level 36")
+                         "7: 4 x 4 baby-step/giant-step linear transform at level 36; "
+                         "8: smaller ring N=2^15 (20+7 primes, dnum 3), batch 8 at level 20")
     ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
                     help="which key variants to time (the headline is always the regenerated one when timed)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,7 +297,7 @@ def main() -> int:
 
 
 def other_workload(args) -> int:
-    """Workloads 3-5: one JSON line each (not the headline); kernel times from the event timer."""
+    """Workloads 3-8: one JSON line each (not the headline); kernel times from the event timer."""
     import numpy as np
     import torch
 
@@ -309,6 +311,9 @@ def other_workload(args) -> int:
     elif args.workload == 7:
         name, unit = ("double-hoisted baby-step/giant-step linear transform, N=2^16, level 36, n1 = n2 = 4 "
                       "(16 diagonals, 3 baby + 3 giant rotation keys g = 5^k)", "transforms/s")
+    elif args.workload == 8:
+        name, unit = ("smaller ring: N=2^15, 20+7 x 32-bit primes, dnum 3, batch 8 ciphertexts at level 20, "
+                      "one rotation key g=5", "key-switches/s")
     else:
         wl = synth.WORKLOADS[args.workload]
         d = synth.draw(args.workload, primes)
@@ -416,6 +421,29 @@ def other_workload(args) -> int:
         diag_bytes = ((n1 * n2 + 2 * (n1 - 1) + 2 * n2) * (LEVEL + K) + (n2 + 1) * 2 * LEVEL) * N * 4
         res["diag_roofline"] = {"bound": "hbm", "achieved_gbs": round(diag_bytes / t_diag / 1e9, 1),
                                 "peak_gbs": HBM_PEAK / 1e9, "frac": round(diag_bytes / t_diag / HBM_PEAK, 4)}
+    elif args.workload == 8:
+        log_n8, l8, k8, d8 = SMALL_RING
+        n8 = 1 << log_n8
+        primes8 = chain_primes(log_n8, BITS, l8 + k8)
+        ctx = Context(log_n8, l8, k8, d8, primes8, max_batch=BATCH)
+        rng = np.random.default_rng(8008)
+        cts = to_device(np.stack([np.stack([synth.residues(rng, primes8[:l8], n8) for _ in range(2)])
+                                  for _ in range(BATCH)]))
+        kb = to_device(synth.uniform_key_rows(8000, primes8, d8, n8))
+        seed = rng.bytes(32)
+        ka = ctx.expand_a(seed)
+        out = torch.empty((BATCH, 2, l8, n8), dtype=torch.int32, device="cuda")
+        for v in variants:
+            fn = (lambda i, v=v: ctx.keyswitch(cts, l8, kb, GALOIS, key_seed=seed if v == "regen" else None,
+                                               key_a=ka if v == "stored" else None, out=out))
+            ms = time_calls(fn, args.steps, args.warmup, torch)
+            ctx.profile(True)
+            for i in range(args.steps):
+                fn(i)
+            ctx.profile(False)
+            prof = ctx.profile_read()
+            res[v] = {"key_switches_per_s": round(BATCH / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
     else:
         ctx = make_context(primes, 16, args)
         kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]

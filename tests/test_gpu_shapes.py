@@ -166,3 +166,24 @@ def test_keyswitch_batches_eight_digits(batch):
             got = host(ctx.keyswitch(gpu(ct), level, dkb, g, key_seed=seed if variant == "regen" else None,
                                      key_a=dka if variant == "stored" else None))
             assert np.array_equal(got, want), (variant, level, first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("variant", ["regen", "stored"])
+def test_smaller_ring_workload_sampled(variant):
+    # the smaller-ring benchmark configuration: N=2^15, 20+7 primes of 32 bits, dnum 3,
+    # batch 8 at level 20, g = 5; ciphertexts 0 and 7 against the oracle
+    announce(f"smaller ring batch 8 level 20 {variant}")
+    shape = (15, 20, 7, 3, 32)
+    pr = Params.make(*shape)
+    ctx = Context(shape[0], shape[1], shape[2], shape[3], pr.primes, 8)
+    rng = np.random.default_rng(8008)
+    ct = np.stack([np.stack([rand_limbs(rng, pr.primes[:20], pr.n) for _ in range(2)]) for _ in range(8)])
+    kb = synth.uniform_key_rows(8000, pr.primes, pr.dnum, pr.n).astype(np.uint64)
+    seed = rng.bytes(32)
+    ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
+    got = host(ctx.keyswitch(gpu(ct), 20, gpu(kb), 5, key_seed=seed if variant == "regen" else None,
+                             key_a=gpu(ka) if variant == "stored" else None))
+    for b in (0, 7):
+        want = oks.keyswitch(pr, ct[b], 20, kb, 5, key_a=ka)
+        assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
+    ctx.close()
