@@ -3,8 +3,11 @@
 The block function is checked at 20 rounds against OpenSSL's ChaCha20 (run as a
 black-box tool, whose 16-byte IV is state words 12..15: block counter then
 nonce); that pins constants, key/counter/nonce placement, the quarter round and
-the byte order.  No ChaCha12 vector is available here: the 12-round output is
-pinned only through the round count being the sole difference.
+the byte order.  No ChaCha12 vector is available here, but the 12-round output
+follows from OpenSSL's 20-round output exactly: the double round P is a
+permutation of the state, ChaCha_r(x) = x + P^(r/2)(x), so
+ChaCha12(x) = x + P^-4(ChaCha20(x) - x), with P^-1 written out below from the
+quarter round's steps undone in reverse order.
 """
 import shutil
 import subprocess
@@ -33,6 +36,55 @@ def _openssl(key: bytes, counter: int, nonce, nbytes: int) -> bytes:
        nblocks=st.integers(1, 5))
 def test_chacha20_matches_openssl(key, counter, nonce, nblocks):
     assert keystream_bytes(key, counter, nonce, nblocks, rounds=20) == _openssl(key, counter, nonce, 64 * nblocks)
+
+
+M32 = 0xFFFFFFFF
+
+
+def _inverse_double_round(s: list) -> None:
+    """Undo one double round in place: the diagonal round, then the column round (its four
+    quarter rounds touch disjoint words, so their order within a round does not matter)."""
+    def rotr(x, r):
+        return ((x >> r) | (x << (32 - r))) & M32
+
+    def inv_quarter(a, b, c, d):
+        s[b] = rotr(s[b], 7) ^ s[c]
+        s[c] = (s[c] - s[d]) & M32
+        s[d] = rotr(s[d], 8) ^ s[a]
+        s[a] = (s[a] - s[b]) & M32
+        s[b] = rotr(s[b], 12) ^ s[c]
+        s[c] = (s[c] - s[d]) & M32
+        s[d] = rotr(s[d], 16) ^ s[a]
+        s[a] = (s[a] - s[b]) & M32
+
+    for a, b, c, d in ((0, 5, 10, 15), (1, 6, 11, 12), (2, 7, 8, 13), (3, 4, 9, 14)):
+        inv_quarter(a, b, c, d)
+    for a, b, c, d in ((0, 4, 8, 12), (1, 5, 9, 13), (2, 6, 10, 14), (3, 7, 11, 15)):
+        inv_quarter(a, b, c, d)
+
+
+def _chacha_from_openssl20(key: bytes, counter: int, nonce, rounds: int) -> list:
+    """ChaCha_rounds block derived from OpenSSL's ChaCha20 block by undoing 10 - rounds/2 double rounds."""
+    x = list(np.frombuffer(b"expand 32-byte k" + key, dtype="<u4").tolist()) + [counter] + list(nonce)
+    out20 = np.frombuffer(_openssl(key, counter, nonce, 64), dtype="<u4").tolist()
+    s = [(o - w) & M32 for o, w in zip(out20, x)]
+    for _ in range(10 - rounds // 2):
+        _inverse_double_round(s)
+    return [(v + w) & M32 for v, w in zip(s, x)]
+
+
+@pytest.mark.skipif(not HAVE_OPENSSL, reason="openssl not on PATH")
+@settings(max_examples=25, deadline=None)
+@given(key=st.binary(min_size=32, max_size=32), counter=st.integers(0, 2**32 - 1),
+       nonce=st.tuples(st.integers(0, 2**32 - 1), st.integers(0, 2**32 - 1), st.integers(0, 2**32 - 1)))
+def test_chacha12_from_openssl_chacha20_by_inverse_rounds(key, counter, nonce):
+    want = _chacha_from_openssl20(key, counter, nonce, 12)
+    got = chacha_blocks(key, counter, nonce[0], nonce[1], nonce[2], rounds=12).tolist()
+    assert got == want
+    # the derivation is not vacuous: other round counts land elsewhere
+    assert chacha_blocks(key, counter, nonce[0], nonce[1], nonce[2], rounds=8).tolist() == \
+        _chacha_from_openssl20(key, counter, nonce, 8)
+    assert got != chacha_blocks(key, counter, nonce[0], nonce[1], nonce[2], rounds=14).tolist()
 
 
 def test_rounds_change_output_and_blocks_are_independent():
