@@ -704,6 +704,8 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
   c->d.K = num_p;
   c->d.dnum = dnum;
   c->d.alpha = alpha;
+  c->d.all_big = 1;
+  for (uint32_t t = 0; t < num_q + num_p; ++t) c->d.all_big &= primes[t] >> 31;
   if (max_batch == 0) {
     *out = c;
     return ok();

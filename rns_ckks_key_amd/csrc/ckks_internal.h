@@ -16,6 +16,7 @@ constexpr uint32_t kMaxRegenBlocks = 256;
 // constant w in Montgomery form wm = w*2^32 mod q and its companion wm*q^-1 mod 2^32.
 struct DevTables {
   uint32_t log_n, n, L, K, dnum, alpha;
+  uint32_t all_big;         // 1: every prime of the chain exceeds 2^31
   const uint32_t* q;        // [L+K]
   const uint32_t* qinv;     // [L+K] q^-1 mod 2^32
   const uint32_t* tw;       // [L+K][N]  psi^brv(k) * 2^32 mod q (companion computed on use)

@@ -2,8 +2,9 @@
 //
 // Residues are canonical, in [0, q), at every kernel boundary.  The primes of a
 // 2^16-point chain all exceed 2^31, so a + b can carry out of 32 bits and the
-// lazy [0, 2q) forms do not fit a word: every add and subtract here reduces
-// fully.  Multiplication by a constant w uses Montgomery's REDC with R = 2^32
+// lazy [0, 2q) forms do not fit a word: add_mod and sub_mod reduce fully.  The
+// forward transforms instead carry any 32-bit representative (lazy_add,
+// lazy_sub) and make it canonical once at the end (canon).  Multiplication by a constant w uses Montgomery's REDC with R = 2^32
 // on a precomputed pair (w~ = w*R mod q, w~ * q^-1 mod R); a sum of up to ~2^31
 // 64-bit products is kept exactly in three words and brought back to [0, q) by
 // two word-steps of REDC (result carries a factor R^-2 that callers fold into a
@@ -41,6 +42,22 @@ __host__ __device__ __forceinline__ uint32_t add_mod(uint32_t a, uint32_t b, uin
   return borrow ? a + b : d;
 }
 
+// Lazy forms, used inside the forward transforms: a value there is any 32-bit
+// representative of its residue (possibly >= q).  For t in [0, q), a + t and a - t
+// stay in [0, 2^32) without a comparison with q: a carry out of a + t is taken back
+// by adding 2^32 - q (giving a + t - q), a borrow of a - t by subtracting it (giving
+// a - t + q).  Valid for every q < 2^32.
+__host__ __device__ __forceinline__ uint32_t lazy_add(uint32_t a, uint32_t t, uint32_t q) {
+  uint32_t s;
+  const bool carry = __builtin_add_overflow(a, t, &s);
+  return carry ? s + (0u - q) : s;
+}
+__host__ __device__ __forceinline__ uint32_t lazy_sub(uint32_t a, uint32_t t, uint32_t q) {
+  uint32_t d;
+  const bool borrow = __builtin_sub_overflow(a, t, &d);
+  return borrow ? d - (0u - q) : d;
+}
+
 // a * w mod q, where (wm, wmq) = (w*2^32 mod q, wm*qinv mod 2^32); any a < 2^32.
 // REDC(a*wm) with the borrow form: (a*wm - m*q)/2^32 = hi(a*wm) - hi(m*q), m = lo(a*wm)*qinv.
 __host__ __device__ __forceinline__ uint32_t mul_const(uint32_t a, uint32_t wm, uint32_t wmq, uint32_t q) {
@@ -56,6 +73,17 @@ __host__ __device__ __forceinline__ uint32_t mont_mul(uint32_t a, uint32_t b, Mo
   const uint32_t hi = umulhi32(a, b);
   const uint32_t t = umulhi32(lo * md.qinv, md.q);
   return sub_mod(hi, t, md.q);
+}
+
+// Canonical residue of a 32-bit representative x.  For q > 2^31, x < 2q and one
+// conditional subtraction does it (min(x, x - q): x - q wraps above x when x < q);
+// otherwise x is multiplied by one = (2^32 mod q, companion), i.e. reduced by REDC.
+__host__ __device__ __forceinline__ uint32_t canon(uint32_t x, uint32_t q, uint32_t one_wm, uint32_t one_wmq) {
+  if (q >> 31) {
+    const uint32_t d = x - q;
+    return d < x ? d : x;
+  }
+  return mul_const(x, one_wm, one_wmq, q);
 }
 
 // Companion of a Montgomery-form constant: wm * q^-1 mod 2^32.

@@ -25,6 +25,16 @@ int main() {
       uint32_t b = it < 49 ? edge[it / 7] : (uint32_t)(rng() % q);
       if (add_mod(a, b, q) != (uint32_t)(((uint64_t)a + b) % q)) { printf("add %u %u %u\n", a, b, q); return 1; }
       if (sub_mod(a, b, q) != (uint32_t)(((uint64_t)a + q - b) % q)) { printf("sub %u %u %u\n", a, b, q); return 1; }
+      // lazy add/subtract of a canonical t to any 32-bit representative, and canonicalisation
+      {
+        const uint32_t x = (uint32_t)rng(), t = b;
+        const uint32_t one_wm = (uint32_t)((((uint64_t)1) << 32) % q);
+        if ((uint64_t)lazy_add(x, t, q) % q != ((uint64_t)x + t) % q) { printf("lazy_add %u %u %u\n", x, t, q); return 1; }
+        if ((uint64_t)lazy_sub(x, t, q) % q != ((uint64_t)x % q + q - t) % q) { printf("lazy_sub %u %u %u\n", x, t, q); return 1; }
+        if (canon(x, q, one_wm, one_wm * qinv) != x % q) { printf("canon %u %u\n", x, q); return 1; }
+        if (canon(a, q, one_wm, one_wm * qinv) != a) { printf("canon canonical %u %u\n", a, q); return 1; }
+        count += 4;
+      }
       // constant multiply, any a < 2^32
       uint32_t araw = it & 1 ? (uint32_t)rng() : a;
       uint32_t wm = (uint32_t)(((uint64_t)b << 32) % q);
