@@ -67,7 +67,8 @@ __host__ __device__ __forceinline__ uint32_t mul_const(uint32_t a, uint32_t wm, 
   return sub_mod(hi, t, q);
 }
 
-// a * b * 2^-32 mod q for a, b < q (REDC of the full product, subtract form).
+// a * b * 2^-32 mod q for b < q and any a < 2^32 (REDC of the full product, subtract
+// form; a * b < q * 2^32 keeps both high words below q).
 __host__ __device__ __forceinline__ uint32_t mont_mul(uint32_t a, uint32_t b, Mod md) {
   const uint32_t lo = a * b;
   const uint32_t hi = umulhi32(a, b);

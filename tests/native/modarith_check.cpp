@@ -33,6 +33,9 @@ int main() {
         if ((uint64_t)lazy_sub(x, t, q) % q != ((uint64_t)x % q + q - t) % q) { printf("lazy_sub %u %u %u\n", x, t, q); return 1; }
         if (canon(x, q, one_wm, one_wm * qinv) != x % q) { printf("canon %u %u\n", x, q); return 1; }
         if (canon(a, q, one_wm, one_wm * qinv) != a) { printf("canon canonical %u %u\n", a, q); return 1; }
+        // Montgomery product with a full 32-bit left operand: x * t * 2^-32 mod q
+        const uint32_t mm = mont_mul(x, t, md);
+        if (mm >= q || (u128)mm * (((u128)1 << 32) % q) % q != (u128)x * t % q) { printf("mont_mul %u %u %u\n", x, t, q); return 1; }
         count += 4;
       }
       // constant multiply, any a < 2^32
