@@ -2,7 +2,9 @@
 
 Ring degrees 2^13..2^15 exercise the other column-pass lengths; dnum = 1 (one
 digit covering every ciphertext prime) and alpha = 1 (one prime per digit) are
-the extreme digit shapes; a partial last digit appears at several levels.
+the extreme digit shapes; a partial last digit appears at several levels.  Rings
+2^15 and 2^16 with 31-bit primes take the column kernels' canonical butterflies
+(chains whose primes all exceed 2^31 take the lazy ones).
 """
 import functools
 
@@ -27,6 +29,8 @@ SHAPES = [  # (log_n, L, K, dnum, bits)
     (12, 4, 4, 1, 30),   # dnum = 1
     (12, 4, 1, 4, 30),   # alpha = 1
     (13, 7, 3, 3, 31),   # partial digits, 31-bit primes
+    (15, 6, 3, 2, 31),   # large rings with primes below 2^31: the canonical-butterfly column kernels
+    (16, 4, 2, 2, 31),
 ]
 
 
