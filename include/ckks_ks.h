@@ -143,9 +143,15 @@ typedef struct {
  * elements), bit-identical to one ckks_keyswitch call per item with batch 1.
  * Items of equal level are processed together, up to min(16, max_batch) per
  * launch sequence, so a decode-shaped stream does not pay one small launch
- * sequence per ciphertext.  items is a host array.  Errors: EINVAL (NULL
- * pointers), ERANGE (an item's level or Galois element), with the item index in
- * ckks_last_error(); nothing is launched if any item is invalid. */
+ * sequence per ciphertext.  The sequences run concurrently on `stream` and up to
+ * three internal streams of the context (default priority, created on the first
+ * call that has more than one sequence), each in its own part of the workspace;
+ * `stream` waits for all of them before the call returns, so work queued on it
+ * afterwards sees every output.  The items must therefore be independent: no
+ * item's out may overlap another item's ct or out.  items is a host array.
+ * Errors: EINVAL (NULL pointers), ERANGE (an item's level or Galois element),
+ * with the item index in ckks_last_error(); nothing is launched if any item is
+ * invalid. */
 ckks_status ckks_keyswitch_multi(const ckks_ctx *ctx, uint32_t n_items, const ckks_ks_item *items, void *stream);
 
 /* The a-half [dnum][L+K][N] that key_seed (host, 32 bytes) regenerates: the stored

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <iterator>
 #include <string>
 #include <vector>
 
@@ -321,6 +322,10 @@ struct ckks_ctx {
   uint32_t* tmpP = nullptr;    // [B][2][K][N]
   uint32_t* conv = nullptr;    // [B][2][L][N]
   uint32_t* tens = nullptr;    // [B][3][L][N]: relinearised pair of a multiply; R and S buffers of a transform
+  // ckks_keyswitch_multi: side streams (default priority, created on first use) and
+  // one event per launch sequence of a call
+  std::vector<hipStream_t> side;
+  std::vector<hipEvent_t> task_ev;
   // per-launch event timer (measurement aid)
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev;     // pool: 2 events per record
@@ -330,6 +335,9 @@ struct ckks_ctx {
 namespace {
 
 constexpr size_t kProfMax = 8192;
+// streams a multi-item key-switch spreads its launch sequences over (the caller's
+// included); four matches the hardware queues HIP gives a process by default
+constexpr uint32_t kMultiStreams = 4;
 
 // Brackets one launch with events on `s` when the context's timer is on.
 struct ProfScope {
@@ -444,6 +452,27 @@ void seed_words(const uint8_t* seed, uint32_t out[8]) {
 }
 
 uint32_t digits_at(const Host& h, uint32_t level) { return (level + h.alpha - 1) / h.alpha; }
+
+// Shifts the context's workspace pointers to start at workspace item `pos` for its
+// lifetime, so that launch sequences on different streams use disjoint item ranges.
+struct WsView {
+  ckks_ctx* c;
+  uint32_t *rowtmp, *ext, *tmpP, *conv;
+  WsView(ckks_ctx* ctx, uint32_t pos) : c(ctx), rowtmp(ctx->rowtmp), ext(ctx->ext), tmpP(ctx->tmpP), conv(ctx->conv) {
+    const Host& h = c->h;
+    const uint64_t N = h.n, p = pos;
+    c->rowtmp += p * std::max(std::max(h.L, h.K), 2u) * N;
+    c->ext += p * h.dnum * (h.L + h.K) * N;
+    c->tmpP += p * 2 * h.K * N;
+    c->conv += p * 2 * h.L * N;
+  }
+  ~WsView() {
+    c->rowtmp = rowtmp;
+    c->ext = ext;
+    c->tmpP = tmpP;
+    c->conv = conv;
+  }
+};
 
 // Steps 1-2: INTT row half of c1 and the fused ModUp conversion into ctx->ext.
 // c1b (optional): c1 is the elementwise product c1 * c1b, formed in the row pass.
@@ -742,6 +771,8 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
 void ckks_ctx_destroy(ckks_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->task_ev) (void)hipEventDestroy(e);
+  for (hipStream_t st : c->side) (void)hipStreamDestroy(st);
   if (c->ws) (void)hipFree(c->ws);
   if (c->dev_tables) (void)hipFree(c->dev_tables);
   delete c;
@@ -1156,41 +1187,138 @@ ckks_status ckks_keyswitch_multi(const ckks_ctx* cc, uint32_t n_items, const ckk
       return fail(st, "item %u: %s", i, m.c_str());
     }
   }
+  {  // outputs overlap neither each other nor any input (the items run concurrently)
+    const uint64_t nb = 2ull * c->h.n * sizeof(uint32_t);
+    std::vector<std::pair<uintptr_t, uintptr_t>> outs(n_items);
+    for (uint32_t i = 0; i < n_items; ++i)
+      outs[i] = {(uintptr_t)items[i].out, (uintptr_t)items[i].out + nb * items[i].level};
+    std::sort(outs.begin(), outs.end());
+    for (uint32_t i = 1; i < n_items; ++i)
+      if (outs[i].first < outs[i - 1].second) return fail(CKKS_EINVAL, "the outputs of two items overlap");
+    for (uint32_t i = 0; i < n_items; ++i) {
+      const uintptr_t lo = (uintptr_t)items[i].ct, hi = lo + nb * items[i].level;
+      auto it = std::lower_bound(outs.begin(), outs.end(), std::make_pair(hi, (uintptr_t)0));
+      if (it != outs.begin() && std::prev(it)->second > lo)
+        return fail(CKKS_EINVAL, "item %u: ct overlaps an item's out", i);
+    }
+  }
   if ((st = check_device(c))) return st;
   hipStream_t s = (hipStream_t)stream;
   const Host& h = c->h;
   const uint64_t N = h.n;
-  const uint32_t chunk = std::min<uint32_t>(c->max_batch, ckks::kMaxGroup);
-  // items of one level run together: one ModUp batch, then the key-using kernels over all their keys
-  std::vector<bool> done(n_items, false);
-  for (uint32_t i0 = 0; i0 < n_items; ++i0) {
-    if (done[i0]) continue;
-    const uint32_t level = items[i0].level;
-    std::vector<uint32_t> group;
-    for (uint32_t i = i0; i < n_items; ++i)
-      if (!done[i] && items[i].level == level) group.push_back(i);
-    for (size_t g0 = 0; g0 < group.size(); g0 += chunk) {
-      const uint32_t m = (uint32_t)std::min<size_t>(chunk, group.size() - g0);
-      const uint32_t* c1s[ckks::kMaxGroup];
-      ckks::KeyRef keys[ckks::kMaxGroup];
-      for (uint32_t k = 0; k < m; ++k) {
-        const ckks_ks_item& it = items[group[g0 + k]];
-        done[group[g0 + k]] = true;
-        c1s[k] = it.ct + (uint64_t)level * N;
-        keys[k] = ckks::KeyRef{};
-        keys[k].b = it.key_b;
-        keys[k].a = it.key_a;
-        if (!it.key_a) seed_words(it.key_seed, keys[k].seed);
-        keys[k].galois = it.galois_elt;
-        keys[k].ct = it.ct;
-        keys[k].out = it.out;
+  const uint32_t B = c->max_batch, chunk = std::min<uint32_t>(B, ckks::kMaxGroup);
+  // Launch sequences: items of equal level, in chunks of at most `chunk`, in the
+  // order of each level's first item.
+  struct Task {
+    uint32_t level, m, idx[ckks::kMaxGroup];
+  };
+  std::vector<Task> tasks;
+  {
+    std::vector<bool> done(n_items, false);
+    for (uint32_t i0 = 0; i0 < n_items; ++i0) {
+      if (done[i0]) continue;
+      Task t{};
+      t.level = items[i0].level;
+      for (uint32_t i = i0; i < n_items; ++i) {
+        if (done[i] || items[i].level != t.level) continue;
+        done[i] = true;
+        t.idx[t.m++] = i;
+        if (t.m == chunk) {
+          tasks.push_back(t);
+          t.m = 0;
+        }
       }
-      hipError_t e = run_modup(c, nullptr, 0, level, m, s, c1s);
-      if (e != hipSuccess) return hip_status(e, "ModUp");
-      e = run_ip_moddown(c, nullptr, 0, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, m, keys, nullptr, false, s,
-                         true);
-      if (e != hipSuccess) return hip_status(e, "inner product / ModDown");
+      if (t.m) tasks.push_back(t);
     }
+  }
+  // The sequences are independent apart from the workspace.  They take item ranges
+  // of the workspace in turn (wrapping round) and are dealt out to the caller's
+  // stream and the side streams in turn; a sequence whose range was last used by a
+  // sequence on another stream waits for that sequence's event.  The caller's
+  // stream finally waits for every side stream, so later calls on it are ordered
+  // after the whole call.
+  const uint32_t S = tasks.size() > 1 && B > 1 ? std::min<uint32_t>(kMultiStreams, (uint32_t)tasks.size()) : 1;
+  while (c->side.size() + 1 < S) {
+    hipStream_t st;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+      return fail(CKKS_EHIP, "hipStreamCreateWithFlags failed");
+    c->side.push_back(st);
+  }
+  if (S > 1)
+    while (c->task_ev.size() < tasks.size() + 1) {
+      hipEvent_t ev;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return fail(CKKS_EHIP, "hipEventCreateWithFlags failed");
+      c->task_ev.push_back(ev);
+    }
+  auto stream_of = [&](uint32_t k) { return k == 0 ? s : c->side[k - 1]; };
+  hipError_t e = hipSuccess;
+  if (S > 1) {  // fork: side streams start after the caller's earlier work
+    hipEvent_t fork = c->task_ev[tasks.size()];
+    if ((e = hipEventRecord(fork, s)) != hipSuccess) return hip_status(e, "hipEventRecord");
+    for (uint32_t k = 1; k < S; ++k)
+      if ((e = hipStreamWaitEvent(stream_of(k), fork, 0)) != hipSuccess) return hip_status(e, "hipStreamWaitEvent");
+  }
+  std::vector<int> owner(B, -1);  // last sequence that used each workspace item
+  uint32_t pos = 0;
+  ckks_status bad = CKKS_OK;
+  for (uint32_t ti = 0; ti < tasks.size() && bad == CKKS_OK; ++ti) {
+    const Task& t = tasks[ti];
+    const uint32_t k = ti % S, level = t.level, m = t.m;
+    hipStream_t st = stream_of(k);
+    if (pos + m > B) pos = 0;
+    if (S > 1) {
+      int last[kMultiStreams];  // newest earlier sequence per other stream on this range
+      for (uint32_t j = 0; j < S; ++j) last[j] = -1;
+      for (uint32_t w = pos; w < pos + m; ++w)
+        if (owner[w] >= 0 && (uint32_t)owner[w] % S != k)
+          last[owner[w] % S] = std::max(last[owner[w] % S], owner[w]);
+      for (uint32_t j = 0; j < S; ++j)
+        if (last[j] >= 0 && (e = hipStreamWaitEvent(st, c->task_ev[last[j]], 0)) != hipSuccess) break;
+      if (e != hipSuccess) {
+        bad = hip_status(e, "hipStreamWaitEvent");
+        break;
+      }
+    }
+    const uint32_t* c1s[ckks::kMaxGroup];
+    ckks::KeyRef keys[ckks::kMaxGroup];
+    for (uint32_t j = 0; j < m; ++j) {
+      const ckks_ks_item& it = items[t.idx[j]];
+      c1s[j] = it.ct + (uint64_t)level * N;
+      keys[j] = ckks::KeyRef{};
+      keys[j].b = it.key_b;
+      keys[j].a = it.key_a;
+      if (!it.key_a) seed_words(it.key_seed, keys[j].seed);
+      keys[j].galois = it.galois_elt;
+      keys[j].ct = it.ct;
+      keys[j].out = it.out;
+    }
+    {
+      WsView view(c, pos);
+      if ((e = run_modup(c, nullptr, 0, level, m, st, c1s)) != hipSuccess) {
+        bad = hip_status(e, "ModUp");
+      } else if ((e = run_ip_moddown(c, nullptr, 0, (uint64_t)h.dnum * (h.L + h.K) * N, level, 1, m, keys, nullptr,
+                                     false, st, true)) != hipSuccess) {
+        bad = hip_status(e, "inner product / ModDown");
+      }
+    }
+    // recorded after a failed launch too, so that the join below stays well formed
+    if (S > 1 && (e = hipEventRecord(c->task_ev[ti], st)) != hipSuccess && bad == CKKS_OK)
+      bad = hip_status(e, "hipEventRecord");
+    for (uint32_t w = pos; w < pos + m; ++w) owner[w] = (int)ti;
+    pos += m;
+  }
+  if (bad != CKKS_OK) {  // keep the message of the first failure
+    std::string msg = g_err;
+    for (uint32_t k = 1; k < S; ++k) (void)hipStreamSynchronize(stream_of(k));
+    g_err = msg;
+    return bad;
+  }
+  // join: the newest sequence of each side stream
+  for (uint32_t k = 1; k < S; ++k) {
+    uint32_t ti = (uint32_t)tasks.size() - 1;
+    while (ti % S != k) --ti;
+    if ((e = hipStreamWaitEvent(s, c->task_ev[ti], 0)) != hipSuccess) return hip_status(e, "hipStreamWaitEvent");
   }
   return ok();
 }

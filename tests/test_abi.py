@@ -131,6 +131,25 @@ def test_host_context_validates_calls_before_any_launch():
     assert lt(n1=3) == ERANGE  # baby key 1 has an even Galois element
     keys[1].galois_elt = 25
     assert lt() == EINVAL and "host-only" in lib.ckks_last_error().decode()
+    span = 2 * 4 * 4096 * 4  # bytes of one [2][4][4096] ciphertext
+
+    def multi(*pairs, level=4):  # (ct, out) addresses of each item
+        arr = (_lib.KsItem * len(pairs))()
+        for it, (ct, out) in zip(arr, pairs):
+            it.ct, it.out, it.key_b, it.level, it.galois_elt = ct, out, 0x1000, level, 5
+        return lib.ckks_keyswitch_multi(h, len(pairs), arr, None)
+
+    base = 0x10000000
+    assert multi((base, base + span), level=5) == ERANGE
+    assert multi((base, base + span), (base + 2 * span, base + span + span // 2)) == EINVAL  # outputs overlap
+    assert "outputs" in lib.ckks_last_error().decode()
+    assert multi((base, base + span), (base + span + 4, base + 3 * span)) == EINVAL  # ct 1 inside out 0
+    assert "item 1" in lib.ckks_last_error().decode()
+    assert multi((base + 3 * span - 4, base + span), (base, base + 2 * span)) == EINVAL  # ct 0 reaches out 1
+    assert "item 0" in lib.ckks_last_error().decode()
+    # touching ranges and shared inputs are fine: the call gets as far as the device check
+    assert multi((base, base + span), (base, base + 2 * span), (base + 4 * span, base + 3 * span)) == EINVAL
+    assert "host-only" in lib.ckks_last_error().decode()
     assert lib.ckks_ctx_set_regen_blocks(h, 63) == ERANGE
     assert lib.ckks_ctx_set_regen_blocks(h, 64) == 0
     with pytest.raises(CkksError) as ei:

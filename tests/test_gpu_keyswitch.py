@@ -8,7 +8,7 @@ import functools
 import numpy as np
 import pytest
 
-from tests.gpu_common import announce, context, first_mismatch, gpu, host, params, rand_limbs
+from tests.gpu_common import announce, context, first_mismatch, gpu, host, params, rand_limbs, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -182,6 +182,42 @@ def test_multi_tiny_chunks_of_sixteen_against_oracle():
     for i, (o, w) in enumerate(zip(outs, want)):
         got = host(o)
         assert np.array_equal(got, w), (i, first_mismatch(got, w))
+
+
+def test_multi_concurrent_sequences_share_a_small_workspace():
+    # max_batch 3: 30 items at levels 4, 3, 2, 1 in an interleaved order make launch
+    # sequences of 1 to 3 items that run on four streams and take the three workspace
+    # items in turn, so most sequences wait for one on another stream.  Every output
+    # against the oracle; then the same call on a side torch stream, twice in a row.
+    announce("multi concurrent sequences max_batch 3")
+    pr = params("tiny")
+    ctx = context("tiny", 3)
+    rng = np.random.default_rng(31)
+    gals = (5, 25, 1, 8191, 125)
+    keys = [oracle_key("tiny", g, 9) for g in gals]
+    levels = [4, 3, 4, 2, 1, 4, 3, 3, 2, 4, 1, 1, 4, 3, 2, 2, 4, 4, 3, 1, 2, 3, 4, 4, 1, 2, 3, 4, 3, 2]
+    items, want = [], []
+    for i, level in enumerate(levels):
+        k = (3 * i) % 5
+        kb, ka, seed = keys[k][0], keys[k][1], keys[k][2]
+        ct = _ct(rng, pr, level, 1)[0]
+        stored = i % 4 == 1
+        items.append((gpu(ct), level, gpu(kb), gals[k], None if stored else seed, gpu(ka) if stored else None, None))
+        want.append(oks.keyswitch(pr, ct, level, kb, gals[k], key_a=ka))
+    outs = ctx.keyswitch_multi(items)
+    for i, (o, w) in enumerate(zip(outs, want)):
+        got = host(o)
+        assert np.array_equal(got, w), (i, levels[i], first_mismatch(got, w))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        outs2 = [torch.full_like(o, -1) for o in outs]
+        items2 = [it[:6] + (o,) for it, o in zip(items, outs2)]
+        ctx.keyswitch_multi(items2)
+        ctx.keyswitch_multi(items2)
+        same = [bool(torch.equal(a, b)) for a, b in zip(outs, outs2)]
+    torch.cuda.synchronize()
+    assert all(same), [i for i, v in enumerate(same) if not v]
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
