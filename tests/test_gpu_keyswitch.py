@@ -238,6 +238,32 @@ def test_keyswitch_boot_batch8_sampled(variant):
     assert oks.switch_error(pr, ct[3], got[3], 36, s, s_src, 5) < oks.noise_bound(pr, 36)
 
 
+@pytest.mark.parametrize("variant", ["regen", "stored"])
+def test_keyswitch_boot_batch37_ragged(variant):
+    # a batch of 37 at level 36 (each wave of the eight-wave kernels loops over four or
+    # five ciphertexts): ciphertexts 0 and 36 against the oracle (regenerated a-half),
+    # and the whole batch bit-identical to calls on slices of 8, 8, 8, 8 and 5
+    announce(f"keyswitch boot batch 37 {variant}")
+    pr = params("boot")
+    ctx = context("boot", 37)
+    kb, ka, seed, s, s_src = oracle_key("boot", 25)
+    rng = np.random.default_rng(37)
+    ct = _ct(rng, pr, 36, 37)
+    dct, dkb = gpu(ct), gpu(kb)
+    kw = dict(key_seed=seed) if variant == "regen" else dict(key_a=gpu(ka))
+    out = ctx.keyswitch(dct, 36, dkb, 25, **kw)
+    for lo, hi in ((0, 8), (8, 16), (16, 24), (24, 32), (32, 37)):
+        part = ctx.keyswitch(dct[lo:hi].contiguous(), 36, dkb, 25, **kw)
+        if not torch.equal(part, out[lo:hi]):
+            a, b = host(out[lo:hi]), host(part)
+            pytest.fail(f"slice {lo}:{hi}: {first_mismatch(a, b)}")
+    if variant == "regen":
+        got = host(out)
+        for b in (0, 36):
+            want = oks.keyswitch(pr, ct[b], 36, kb, 25, key_a=ka)
+            assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
+
+
 def test_keyswitch_boot_partial_digit_level():
     announce("keyswitch boot level 13 and 4")
     pr = params("boot")
