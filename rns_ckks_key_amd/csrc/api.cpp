@@ -1238,19 +1238,23 @@ ckks_status ckks_keyswitch_multi(const ckks_ctx* cc, uint32_t n_items, const ckk
   // stream finally waits for every side stream, so later calls on it are ordered
   // after the whole call.
   const uint32_t S = tasks.size() > 1 && B > 1 ? std::min<uint32_t>(kMultiStreams, (uint32_t)tasks.size()) : 1;
-  while (c->side.size() + 1 < S) {
-    hipStream_t st;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
-      return fail(CKKS_EHIP, "hipStreamCreateWithFlags failed");
-    c->side.push_back(st);
-  }
-  if (S > 1)
-    while (c->task_ev.size() < tasks.size() + 1) {
-      hipEvent_t ev;
-      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
-        return fail(CKKS_EHIP, "hipEventCreateWithFlags failed");
-      c->task_ev.push_back(ev);
+  if (S > 1 && (c->side.size() + 1 < S || c->task_ev.size() < tasks.size() + 1)) {
+    // created on the context's device, whichever is current
+    int cur = c->device;
+    if (hipGetDevice(&cur) != hipSuccess || (cur != c->device && hipSetDevice(c->device) != hipSuccess))
+      return fail(CKKS_EHIP, "cannot select the context's device");
+    hipError_t ce = hipSuccess;
+    while (c->side.size() + 1 < S && ce == hipSuccess) {
+      hipStream_t st;
+      if ((ce = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) == hipSuccess) c->side.push_back(st);
     }
+    while (c->task_ev.size() < tasks.size() + 1 && ce == hipSuccess) {
+      hipEvent_t ev;
+      if ((ce = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) == hipSuccess) c->task_ev.push_back(ev);
+    }
+    if (cur != c->device) (void)hipSetDevice(cur);
+    if (ce != hipSuccess) return hip_status(ce, "creating the side streams and events");
+  }
   auto stream_of = [&](uint32_t k) { return k == 0 ? s : c->side[k - 1]; };
   hipError_t e = hipSuccess;
   if (S > 1) {  // fork: side streams start after the caller's earlier work
