@@ -139,6 +139,8 @@ def test_host_context_validates_calls_before_any_launch():
             it.ct, it.out, it.key_b, it.level, it.galois_elt = ct, out, 0x1000, level, 5
         return lib.ckks_keyswitch_multi(h, len(pairs), arr, None)
 
+    assert lib.ckks_keyswitch_multi(h, 0, None, None) == 0  # an empty stream is a no-op
+    assert lib.ckks_keyswitch_multi(h, 2, None, None) == EINVAL
     base = 0x10000000
     assert multi((base, base + span), level=5) == ERANGE
     assert multi((base, base + span), (base + 2 * span, base + span + span // 2)) == EINVAL  # outputs overlap
