@@ -25,7 +25,9 @@
  *    absolute prime t, so one key serves every level.  The a-half is exactly the
  *    ChaCha12 expansion of the key's 32-byte seed (see ckks_expand_a).
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL
- *    is the default stream) and never synchronises the host.  Calls on one
+ *    is the default stream) and never synchronises the host (the one exception:
+ *    ckks_keyswitch_multi waits for its internal streams when a launch fails
+ *    part-way, before it returns the error).  Calls on one
  *    context share its workspace: calls on different streams must not overlap
  *    (use one context per stream).  Output buffers must not alias inputs.
  *  - Arguments are validated before anything is launched; on failure nothing is
@@ -252,7 +254,8 @@ typedef enum {
 } ckks_kernel_class;
 
 /* Measurement aid: while enabled, every launch of this context is bracketed by
- * two HIP events recorded on the call's stream (at most 8192 launches are kept;
+ * two HIP events recorded on the stream it is launched on (the call's stream, or
+ * an internal one of ckks_keyswitch_multi; at most 8192 launches are kept;
  * later ones are not timed).  Enabling clears earlier records; disabling keeps
  * them for ckks_profile_read.  Errors: EINVAL (NULL or host-only context). */
 ckks_status ckks_profile_enable(ckks_ctx *ctx, int enable);
