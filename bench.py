@@ -456,7 +456,8 @@ def other_workload(args) -> int:
                 k = d.key_index[c]
                 items.append((cts[c], d.levels[c], kbs[k], wl.galois[k], d.keys[k].seed if v == "regen" else None,
                               kas[k] if v == "stored" else None, outs[c]))
-            # one multi-item call: ciphertexts of equal level share launches
+            # one multi-item call: ciphertexts of equal level share launches, and the launch
+            # sequences of different levels run concurrently on the library's four streams
             ms = time_calls(lambda i, items=items: ctx.keyswitch_multi(items), args.steps, args.warmup, torch)
             # one call per ciphertext, for comparison
             ms1 = time_calls(lambda i, items=items: [ctx.keyswitch(it[0][None], it[1], it[2], it[3], key_seed=it[4],
