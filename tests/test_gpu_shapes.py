@@ -191,3 +191,24 @@ def test_smaller_ring_workload_sampled(variant):
         want = oks.keyswitch(pr, ct[b], 20, kb, 5, key_a=ka)
         assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
     ctx.close()
+
+
+@pytest.mark.parametrize("shape", [(15, 36, 12, 3, 32), (15, 36, 12, 3, 31), (16, 36, 12, 3, 31)])
+def test_wide_conversion_workgroups_other_rings(shape):
+    # batch 8 at level 36: both conversions have 36 targets x 16 columns per
+    # workgroup and take 512-thread workgroups; ring 2^15 (32-bit primes: lazy
+    # column butterflies; 31-bit: canonical) and ring 2^16 with 31-bit primes cover
+    # the instantiations the main chain does not; ciphertexts 0 and 7 against the oracle
+    announce(f"wide conversion shape {shape} batch 8 level 36")
+    pr = Params.make(*shape)
+    ctx = Context(shape[0], shape[1], shape[2], shape[3], pr.primes, 8)
+    rng = np.random.default_rng(3600 + shape[0] + shape[4])
+    ct = np.stack([np.stack([rand_limbs(rng, pr.primes[:36], pr.n) for _ in range(2)]) for _ in range(8)])
+    kb = synth.uniform_key_rows(3601, pr.primes, pr.dnum, pr.n).astype(np.uint64)
+    seed = rng.bytes(32)
+    ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
+    got = host(ctx.keyswitch(gpu(ct), 36, gpu(kb), 25, key_seed=seed))
+    for b in (0, 7):
+        want = oks.keyswitch(pr, ct[b], 36, kb, 25, key_a=ka)
+        assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
+    ctx.close()
