@@ -150,6 +150,26 @@ def test_hoisted_multiply_and_bsgs_both_paths_agree():
     assert_same(a, b, "bsgs")
 
 
+def test_multi_item_both_paths_agree():
+    # six items at four levels: launch sequences on several streams, matrix-core conversions in each
+    pr = params("boot")
+    rng = np.random.default_rng(8)
+    kbs = [gpu(key_rows(9200 + k)) for k in range(2)]
+    announce("mfma multi-item 6 items")
+    items = []
+    for i, level in enumerate((36, 24, 13, 36, 5, 24)):
+        ct = gpu(np.stack([rand_limbs(rng, pr.primes[:level], pr.n) for _ in range(2)]))
+        out = torch.empty((2, level, pr.n), dtype=torch.int32, device="cuda")
+        items.append((ct, level, kbs[i % 2], pow(5, i + 1, 2 * pr.n), bytes([i]) * 32, None, out))
+
+    def run(ctx):
+        ctx.keyswitch_multi(items)
+        return torch.cat([it[6].flatten() for it in items])
+
+    a, b = both_paths(run)
+    assert_same(a, b, "multi")
+
+
 def test_matrix_cores_refused_for_other_shapes():
     announce("mfma unsupported shape")
     pr = params("tiny")

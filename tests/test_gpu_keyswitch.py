@@ -218,6 +218,10 @@ def test_multi_concurrent_sequences_share_a_small_workspace():
         same = [bool(torch.equal(a, b)) for a, b in zip(outs, outs2)]
     torch.cuda.synchronize()
     assert all(same), [i for i, v in enumerate(same) if not v]
+    # max_batch 1: one item per launch sequence, all on the caller's stream in one workspace item
+    outs1 = context("tiny", 1).keyswitch_multi([it[:6] + (None,) for it in items])
+    same = [bool(torch.equal(a, b)) for a, b in zip(outs, outs1)]
+    assert all(same), [i for i, v in enumerate(same) if not v]
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
