@@ -79,6 +79,35 @@ __host__ __device__ __forceinline__ uint32_t mont_mul(uint32_t a, uint32_t b, Mo
 // Canonical residue of a 32-bit representative x.  For q > 2^31, x < 2q and one
 // conditional subtraction does it (min(x, x - q): x - q wraps above x when x < q);
 // otherwise x is multiplied by one = (2^32 mod q, companion), i.e. reduced by REDC.
+// a - b*c*2^-32 (mod q) for any 32-bit a and b and c < q, as a 32-bit representative
+// (a lazy value).  The Montgomery product's two reduction cases fold into the
+// subtraction's: with u = t - hi (hi - t is the unreduced product, in (-q, q)), the
+// word sum a + u is corrected by +q if u wrapped and by -q (adding nq = 2^32 - q)
+// if the sum carried.  nq is an argument so that a caller can keep the compiler
+// from turning the second correction into a subtraction (three-operand add).
+__host__ __device__ __forceinline__ uint32_t lazy_sub_mont(uint32_t a, uint32_t b, uint32_t c, Mod md,
+                                                           uint32_t nq) {
+  const uint32_t lo = b * c;
+  const uint32_t hi = umulhi32(b, c);
+  const uint32_t t = umulhi32(lo * md.qinv, md.q);
+  uint32_t u, s;
+  const bool neg = __builtin_sub_overflow(t, hi, &u);
+  const bool carry = __builtin_add_overflow(a, u, &s);
+  return s + (neg ? md.q : 0u) + (carry ? nq : 0u);
+}
+
+// a + b*c*2^-32 (mod q), the same way: u = hi - t, corrected as in lazy_sub_mont.
+__host__ __device__ __forceinline__ uint32_t lazy_add_mont(uint32_t a, uint32_t b, uint32_t c, Mod md,
+                                                           uint32_t nq) {
+  const uint32_t lo = b * c;
+  const uint32_t hi = umulhi32(b, c);
+  const uint32_t t = umulhi32(lo * md.qinv, md.q);
+  uint32_t u, s;
+  const bool neg = __builtin_sub_overflow(hi, t, &u);
+  const bool carry = __builtin_add_overflow(a, u, &s);
+  return s + (neg ? md.q : 0u) + (carry ? nq : 0u);
+}
+
 __host__ __device__ __forceinline__ uint32_t canon(uint32_t x, uint32_t q, uint32_t one_wm, uint32_t one_wmq) {
   if (q >> 31) {
     const uint32_t d = x - q;

@@ -36,7 +36,22 @@ int main() {
         // Montgomery product with a full 32-bit left operand: x * t * 2^-32 mod q
         const uint32_t mm = mont_mul(x, t, md);
         if (mm >= q || (u128)mm * (((u128)1 << 32) % q) % q != (u128)x * t % q) { printf("mont_mul %u %u %u\n", x, t, q); return 1; }
-        count += 4;
+        // the accumulation step of the final inner-product pass, x - y * t * 2^-32 for any
+        // 32-bit x and y: ls * 2^32 = x * 2^32 - y * t (mod q), word edges included
+        const uint32_t wedge[] = {0u, 1u, q - 1, q, q + 1, 0xffffffffu, 0x80000000u};
+        const uint32_t xs = it < 49 ? wedge[it % 7] : x, ys = it < 49 ? wedge[it / 7] : (uint32_t)rng();
+        const uint32_t ls = lazy_sub_mont(xs, ys, t, md, 0u - q);
+        const u128 r32 = ((u128)1 << 32) % q;
+        if (((u128)ls * r32 + (u128)ys * t) % q != (u128)xs * r32 % q) {
+          printf("lazy_sub_mont %u %u %u %u\n", xs, ys, t, q);
+          return 1;
+        }
+        const uint32_t la = lazy_add_mont(xs, ys, t, md, 0u - q);  // la * 2^32 = x * 2^32 + y * t
+        if (((u128)la * r32) % q != ((u128)xs * r32 + (u128)ys * t) % q) {
+          printf("lazy_add_mont %u %u %u %u\n", xs, ys, t, q);
+          return 1;
+        }
+        count += 6;
       }
       // constant multiply, any a < 2^32
       uint32_t araw = it & 1 ? (uint32_t)rng() : a;
