@@ -1,9 +1,9 @@
 /* ckks_ks.h - RNS-CKKS hybrid key-switching on one AMD Instinct MI355X (gfx950).
  *
- * The method: half of every key-switching key is uniformly random, so instead
- * of being stored it can be regenerated inside the kernels that use the key by a
- * counter-mode ChaCha12 expander, halving key storage; the chain is an RNS CKKS
- * chain of 32-bit primes (Perseus summary on ai4snews, "Interpretation"
+ * The method: one half of a key-switching key is uniformly random, so only its
+ * 32-byte seed is kept and the kernels that consume the key rebuild that half
+ * with ChaCha12 in counter mode, which cuts the key's memory in two; the chain is
+ * RNS CKKS over 32-bit primes (Perseus summary on ai4snews, "Interpretation"
  * paragraph 2; the Perseus abstract names this in-kernel key regeneration as its
  * backend-level change).  The rest of the path is textbook hybrid key-switching
  * (Han and Ki, CT-RSA 2020) with fast base conversion (Bajard et al., SAC 2016)
@@ -84,25 +84,40 @@ ckks_status ckks_ctx_info(const ckks_ctx *ctx, uint32_t *n_out, uint32_t *num_q_
 
 /* Forward negacyclic NTT, in place, of data[batch][n_limbs][N] (coefficients in
  * natural order in, NTT domain out); limb i of each item is taken modulo chain
- * prime first_prime + i.  Errors: ERANGE if first_prime + n_limbs > L+K or batch
- * or n_limbs is 0. */
+ * prime first_prime + i.  The pages name the key-switching key and a 32-bit RNS
+ * chain (Perseus summary on ai4snews, "Interpretation" paragraph 2) but fix no
+ * transform; the reading taken is the textbook one: entry j of the output is the
+ * input polynomial evaluated at psi^(2*brv(j)+1), psi the smallest x >= 2 with
+ * x^N = -1 mod q (merged-twist Cooley-Tukey, Longa and Naehrig 2016).  data is
+ * caller-owned and is overwritten.  Errors: EINVAL (NULL ctx or data, host-only
+ * context), ERANGE if first_prime + n_limbs > L+K, or batch or n_limbs is 0. */
 ckks_status ckks_ntt_fwd(const ckks_ctx *ctx, uint32_t *data, uint32_t first_prime, uint32_t n_limbs,
                          uint32_t batch, void *stream);
-/* Inverse of ckks_ntt_fwd (includes the factor N^-1). */
+/* Inverse of ckks_ntt_fwd, in place (Gentleman-Sande, includes the factor N^-1):
+ * NTT domain in, coefficients out.  Same reading, ownership and errors. */
 ckks_status ckks_ntt_inv(const ckks_ctx *ctx, uint32_t *data, uint32_t first_prime, uint32_t n_limbs,
                          uint32_t batch, void *stream);
 
 /* ModUp: extended digits of c1[batch][level][N] (NTT domain).  digits is
  * [batch][d_l][level+K][N]: limb e of digit j is over prime e (e < level) or
  * p_{e-level}; for a prime of digit j it is c1's own limb, otherwise the NTT of
- * the fast base conversion of digit j's coefficients, without overflow
- * correction.  Errors: ERANGE for level outside 1..L or batch outside 1..max_batch. */
+ * the fast base conversion of digit j's coefficients.  The pages give no steps
+ * for key-switching beyond its key (Perseus summary on ai4snews, "Interpretation"
+ * paragraph 2); the reading taken is hybrid key-switching's ModUp (Han and Ki,
+ * CT-RSA 2020) with fast base conversion without overflow correction (Bajard et
+ * al., SAC 2016): the multiple u*Q_j (0 <= u < digit size) stays in, and cancels
+ * against the key's gadget.  Caller-owned buffers; digits must not overlap c1.
+ * Errors: EINVAL (NULL, overlap, host-only context), ERANGE for level outside
+ * 1..L or batch outside 1..max_batch. */
 ckks_status ckks_modup(const ckks_ctx *ctx, const uint32_t *c1, uint32_t level, uint32_t *digits,
                        uint32_t batch, void *stream);
 
 /* ModDown: out[batch][level][N] = (x_i - NTT(conv_{P->q_i}(INTT(x_P)))) * P^-1 mod q_i for
- * x[batch][level+K][N] (level ciphertext limbs then K special limbs, NTT domain);
- * floor-type: no P/2 offset, conversion overflow left in.  Errors as ckks_modup. */
+ * x[batch][level+K][N] (level ciphertext limbs then K special limbs, NTT domain).
+ * Reading taken (the pages give no steps): floor-type ModDown of hybrid
+ * key-switching (Han and Ki, CT-RSA 2020): no P/2 offset, and the conversion's
+ * overflow v*P (0 <= v < K) left in.  out must not overlap x.  Errors: EINVAL
+ * (NULL, overlap, host-only context), ERANGE (level, batch). */
 ckks_status ckks_moddown(const ckks_ctx *ctx, const uint32_t *x, uint32_t level, uint32_t *out,
                          uint32_t batch, void *stream);
 
@@ -112,7 +127,8 @@ ckks_status ckks_moddown(const ckks_ctx *ctx, const uint32_t *x, uint32_t level,
  * with d_j the ModUp digits of c1 and sigma applied in the NTT domain after ModUp.
  * key_a == NULL: the a-half is regenerated in-kernel from key_seed (host, 32
  * bytes); otherwise key_a is the stored a-half and key_seed is ignored (may be
- * NULL).  Errors: EINVAL (NULL ct/key_b/out, or both key_a and key_seed NULL),
+ * NULL).  out must not overlap ct, key_b or key_a.  Errors: EINVAL (NULL
+ * ct/key_b/out, both key_a and key_seed NULL, an overlap, host-only context),
  * ERANGE (level, batch, even or out-of-range galois_elt). */
 ckks_status ckks_keyswitch(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, const uint32_t *key_b,
                            const uint8_t *key_seed, const uint32_t *key_a, uint32_t galois_elt,
@@ -124,7 +140,7 @@ ckks_status ckks_keyswitch(const ckks_ctx *ctx, const uint32_t *ct, uint32_t lev
  * key_b, galois_elts and key_seeds are host arrays (key_b holds device
  * pointers; key_seeds is 32*n_keys bytes); key_a is NULL (all regenerated) or a
  * host array of device pointers whose NULL entries are regenerated.
- * 1 <= n_keys <= 64.  Errors as ckks_keyswitch. */
+ * 1 <= n_keys <= 64; out must not overlap ct or any key.  Errors as ckks_keyswitch. */
 ckks_status ckks_keyswitch_hoisted(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, uint32_t n_keys,
                                    const uint32_t *const *key_b, const uint8_t *key_seeds,
                                    const uint32_t *const *key_a, const uint32_t *galois_elts,
@@ -245,12 +261,11 @@ typedef enum {
   CKKS_K_IP_FINAL = 5,     /* inner product over the ciphertext primes + end of ModDown */
   CKKS_K_EXPAND = 6,       /* standalone a-half expansion */
   CKKS_K_MODDOWN_FINAL = 7,/* end of a standalone ModDown: row NTT fused with (x - .) * P^-1 */
-  CKKS_K_TENSOR = 8,       /* reserved: the tensor product is formed inside the relinearisation's kernels */
-  CKKS_K_RESCALE_CONV = 9, /* rescale column passes: INTT of the dropped limb; its reduction and NTT per q_i */
-  CKKS_K_RESCALE_FINAL = 10,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
-  CKKS_K_BABY = 11,        /* baby steps of a linear transform in the extended basis */
-  CKKS_K_DIAG = 12,        /* diagonal sums of a linear transform, and the sum of its giant steps */
-  CKKS_K_CLASSES = 13
+  CKKS_K_RESCALE_CONV = 8, /* rescale column passes: INTT of the dropped limb; its reduction and NTT per q_i */
+  CKKS_K_RESCALE_FINAL = 9,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
+  CKKS_K_BABY = 10,        /* baby steps of a linear transform in the extended basis */
+  CKKS_K_DIAG = 11,        /* diagonal sums of a linear transform, and the sum of its giant steps */
+  CKKS_K_CLASSES = 12
 } ckks_kernel_class;
 
 /* Measurement aid: while enabled, every launch of this context is bracketed by

@@ -80,7 +80,7 @@ _SIGS = {
 }
 
 KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final",
-                  "tensor", "rescale_conv", "rescale_final", "baby", "diag"]
+                  "rescale_conv", "rescale_final", "baby", "diag"]
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

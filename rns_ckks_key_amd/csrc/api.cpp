@@ -440,6 +440,24 @@ ckks_status check_galois(const ckks_ctx* c, uint32_t g) {
   return CKKS_OK;
 }
 
+// Whether word ranges [a, a + na) and [b, b + nb) overlap (a NULL range never does).
+bool overlaps(const uint32_t* a, uint64_t na, const uint32_t* b, uint64_t nb) {
+  return a && b && a < b + nb && b < a + na;
+}
+
+// A key-switch's output (out_words words) overlaps neither its ciphertexts
+// ct[batch][2][level][N] nor the key halves [dnum][L+K][N] (the kernels read
+// them after the first outputs are written).
+ckks_status check_keyswitch_out(const ckks_ctx* c, const uint32_t* ct, uint32_t level, uint32_t batch,
+                                const uint32_t* key_b, const uint32_t* key_a, const uint32_t* out,
+                                uint64_t out_words) {
+  const uint64_t N = c->h.n, key_words = (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N;
+  if (overlaps(ct, (uint64_t)batch * 2 * level * N, out, out_words)) return fail(CKKS_EINVAL, "out overlaps ct");
+  if (overlaps(key_b, key_words, out, out_words)) return fail(CKKS_EINVAL, "out overlaps key_b");
+  if (overlaps(key_a, key_words, out, out_words)) return fail(CKKS_EINVAL, "out overlaps key_a");
+  return CKKS_OK;
+}
+
 ckks_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(CKKS_EHIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -474,19 +492,34 @@ struct WsView {
   }
 };
 
-// Steps 1-2: INTT row half of c1 and the fused ModUp conversion into ctx->ext.
+// Workspace of one key-switch launch sequence: c1 after the row half of INTT
+// (rowtmp, item stride level*N), the extended digits (ext, item stride ext_item),
+// the special part after the row INTT (tmpP, item stride 2K*N) and the converted
+// special part (conv, item stride 2*level*N).  By default the context's own.
+struct Ws {
+  uint32_t *rowtmp, *ext, *tmpP, *conv;
+  uint64_t ext_item;
+};
+
+Ws ctx_ws(const ckks_ctx* c) {
+  return Ws{c->rowtmp, c->ext, c->tmpP, c->conv, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * c->h.n};
+}
+
+// Steps 1-2: INTT row half of c1 and the fused ModUp conversion into the workspace's ext.
 // c1b (optional): c1 is the elementwise product c1 * c1b, formed in the row pass.
 hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, uint32_t level, uint32_t items,
-                     hipStream_t s, const uint32_t* const* c1_items = nullptr, const uint32_t* c1b = nullptr) {
+                     hipStream_t s, const uint32_t* const* c1_items = nullptr, const uint32_t* c1b = nullptr,
+                     const Ws* wsp = nullptr) {
   const Host& h = c->h;
   const uint64_t N = h.n;
+  const Ws w = wsp ? *wsp : ctx_ws(c);
   ckks::RowArgs r{};
   r.src = c1;
   if (c1_items) {  // one pointer per item (at most kMaxGroup)
     r.use_srcs = 1;
     for (uint32_t i = 0; i < items; ++i) r.srcs[i] = c1_items[i];
   }
-  r.dst = c->rowtmp;
+  r.dst = w.rowtmp;
   r.src2 = c1b;
   r.src_item_stride = c1_item_stride;
   r.dst_item_stride = (uint64_t)level * N;
@@ -501,11 +534,11 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
   }
   if (e != hipSuccess) return e;
   ckks::ConvArgs a{};
-  a.src = c->rowtmp;
+  a.src = w.rowtmp;
   a.src_item = (uint64_t)level * N;
   a.src_y = (uint64_t)h.alpha * N;
-  a.dst = c->ext;
-  a.dst_item = (uint64_t)h.dnum * (h.L + h.K) * N;
+  a.dst = w.ext;
+  a.dst_item = w.ext_item;
   a.dst_y = (uint64_t)(h.L + h.K) * N;
   a.src_prime0 = 0;
   a.src_prime_step = h.alpha;
@@ -526,26 +559,27 @@ hipError_t run_modup(ckks_ctx* c, const uint32_t* c1, uint64_t c1_item_stride, u
   }
   ProfScope p(c, CKKS_K_MODUP_CONV, s);
   return ckks::launch_conv(c->d, a, digits_at(h, level), items, s);
-  return hipSuccess;
 }
 
-// Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (ctx->ext already filled).
+// Steps 3-5 for `n_keys` key groups of `n_ct` ciphertexts each (the workspace's ext already
+// filled; ciphertext c's digits at ext + c * ext_stride).
 hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, uint64_t ext_stride,
                           uint32_t level, uint32_t n_ct, uint32_t n_keys, const ckks::KeyRef* keys, uint32_t* out,
                           bool digits_ntt, hipStream_t s, bool per_group = false,
-                          const uint32_t* ty = nullptr) {
+                          const uint32_t* ty = nullptr, const Ws* wsp = nullptr) {
   const Host& h = c->h;
   const uint64_t N = h.n;
+  const Ws w = wsp ? *wsp : ctx_ws(c);
   ckks::IpArgs ip{};
   ip.level = level;
   ip.nd = digits_at(h, level);
   ip.n_ct = n_ct;
-  ip.ext = c->ext;
+  ip.ext = w.ext;
   ip.ext_ct_stride = ext_stride;
   ip.ct = ct;
   ip.ct_ct_stride = ct_stride;
-  ip.tmpP = c->tmpP;
-  ip.conv = c->conv;
+  ip.tmpP = w.tmpP;
+  ip.conv = w.conv;
   ip.out = out;
   ip.regen_blocks = c->regen_blocks;
   ip.digits_ntt = digits_ntt ? 1u : 0u;
@@ -560,10 +594,10 @@ hipError_t run_ip_moddown(ckks_ctx* c, const uint32_t* ct, uint64_t ct_stride, u
   }
   if (e != hipSuccess) return e;
   ckks::ConvArgs a{};
-  a.src = c->tmpP;
+  a.src = w.tmpP;
   a.src_item = 2ull * h.K * N;
   a.src_y = (uint64_t)h.K * N;
-  a.dst = c->conv;
+  a.dst = w.conv;
   a.dst_item = 2ull * level * N;
   a.dst_y = (uint64_t)level * N;
   a.src_prime0 = h.L;
@@ -673,6 +707,35 @@ hipError_t run_moddown(ckks_ctx* c, const uint32_t* x, uint64_t x_item, uint32_t
   f.cmb_factor = c->d.md_fin_pl;
   ProfScope p(c, CKKS_K_MODDOWN_FINAL, s);
   return ckks::launch_row(c->d, f, true, items, s);
+}
+
+// Argument checks of a key-switch call other than the batch limit and the device.
+ckks_status check_keyswitch_args(const ckks_ctx* c, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
+                                 const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt,
+                                 const uint32_t* out, uint32_t batch) {
+  ckks_status st;
+  if (!ct || !key_b || !out) return fail(CKKS_EINVAL, "ct, key_b or out is NULL");
+  if (!key_a && !key_seed) return fail(CKKS_EINVAL, "need key_a or key_seed");
+  if ((st = check_level(c, level)) || (st = check_galois(c, galois_elt))) return st;
+  return check_keyswitch_out(c, ct, level, batch, key_b, key_a, out, (uint64_t)batch * 2 * level * c->h.n);
+}
+
+// The launch sequence of one batched key-switch, in the workspace `wsp` (the
+// context's when NULL).
+ckks_status keyswitch_run(ckks_ctx* c, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
+                          const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt, uint32_t* out,
+                          uint32_t batch, hipStream_t s, const Ws* wsp) {
+  const uint64_t N = c->h.n;
+  const Ws w = wsp ? *wsp : ctx_ws(c);
+  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 2ull * level * N, level, batch, s, nullptr, nullptr, &w);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  ckks::KeyRef k{};
+  k.b = key_b;
+  k.a = key_a;
+  if (!key_a) seed_words(key_seed, k.seed);
+  k.galois = galois_elt;
+  e = run_ip_moddown(c, ct, 2ull * level * N, w.ext_item, level, batch, 1, &k, out, false, s, false, nullptr, &w);
+  return hip_status(e, "inner product / ModDown");
 }
 
 }  // namespace
@@ -875,10 +938,13 @@ ckks_status ckks_modup(const ckks_ctx* cc, const uint32_t* c1, uint32_t level, u
   ckks_status st = check_ctx(c);
   if (st) return st;
   if (!c1 || !digits) return fail(CKKS_EINVAL, "c1 or digits is NULL");
-  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_device(c))) return st;
-  hipStream_t s = (hipStream_t)stream;
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch))) return st;
   const Host& h = c->h;
   const uint64_t N = h.n, El = level + h.K;
+  if (overlaps(c1, (uint64_t)batch * level * N, digits, (uint64_t)batch * digits_at(h, level) * El * N))
+    return fail(CKKS_EINVAL, "digits overlaps c1");
+  if ((st = check_device(c))) return st;
+  hipStream_t s = (hipStream_t)stream;
   hipError_t e = run_modup(c, c1, (uint64_t)level * N, level, batch, s);
   if (e != hipSuccess) return hip_status(e, "ModUp");
   const uint32_t d = digits_at(h, level);
@@ -910,8 +976,11 @@ ckks_status ckks_moddown(const ckks_ctx* cc, const uint32_t* x, uint32_t level, 
   ckks_status st = check_ctx(c);
   if (st) return st;
   if (!x || !out) return fail(CKKS_EINVAL, "x or out is NULL");
-  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_device(c))) return st;
+  if ((st = check_level(c, level)) || (st = check_batch(c, batch))) return st;
   const uint64_t N = c->h.n;
+  if (overlaps(x, (uint64_t)batch * (level + c->h.K) * N, out, (uint64_t)batch * level * N))
+    return fail(CKKS_EINVAL, "out overlaps x");
+  if ((st = check_device(c))) return st;
   return hip_status(run_moddown(c, x, (uint64_t)(level + c->h.K) * N, level, out, (uint64_t)level * N, batch,
                                 (hipStream_t)stream),
                     "ModDown");
@@ -923,23 +992,10 @@ ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t leve
   ckks_ctx* c = const_cast<ckks_ctx*>(cc);
   ckks_status st = check_ctx(c);
   if (st) return st;
-  if (!ct || !key_b || !out) return fail(CKKS_EINVAL, "ct, key_b or out is NULL");
-  if (!key_a && !key_seed) return fail(CKKS_EINVAL, "need key_a or key_seed");
-  if ((st = check_level(c, level)) || (st = check_batch(c, batch)) || (st = check_galois(c, galois_elt)) ||
-      (st = check_device(c)))
+  if ((st = check_keyswitch_args(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch)) ||
+      (st = check_batch(c, batch)) || (st = check_device(c)))
     return st;
-  hipStream_t s = (hipStream_t)stream;
-  const uint64_t N = c->h.n;
-  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 2ull * level * N, level, batch, s);
-  if (e != hipSuccess) return hip_status(e, "ModUp");
-  ckks::KeyRef k{};
-  k.b = key_b;
-  k.a = key_a;
-  if (!key_a) seed_words(key_seed, k.seed);
-  k.galois = galois_elt;
-  e = run_ip_moddown(c, ct, 2ull * level * N, (uint64_t)c->h.dnum * (c->h.L + c->h.K) * N, level, batch, 1, &k,
-                     out, false, s);
-  return hip_status(e, "inner product / ModDown");
+  return keyswitch_run(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch, (hipStream_t)stream, nullptr);
 }
 
 }  // extern "C"
@@ -994,9 +1050,6 @@ hipError_t run_rescale(ckks_ctx* c, const uint32_t* src, uint32_t level, uint32_
   return ckks::launch_row(c->d, f, true, items, s);
 }
 
-bool overlaps(const uint32_t* a, uint64_t na, const uint32_t* b, uint64_t nb) {
-  return a < b + nb && b < a + na;
-}
 
 }  // namespace
 
@@ -1151,6 +1204,10 @@ ckks_status ckks_keyswitch_hoisted(const ckks_ctx* cc, const uint32_t* ct, uint3
     if ((!key_a || !key_a[k]) && !key_seeds) return fail(CKKS_EINVAL, "key %u has neither key_a nor a seed", k);
     if ((st = check_galois(c, galois_elts[k]))) return st;
   }
+  for (uint32_t k = 0; k < n_keys; ++k)
+    if ((st = check_keyswitch_out(c, ct, level, 1, key_b[k], key_a ? key_a[k] : nullptr, out,
+                                  (uint64_t)n_keys * 2 * level * c->h.n)))
+      return st;
   if ((st = check_device(c))) return st;
   hipStream_t s = (hipStream_t)stream;
   const uint64_t N = c->h.n;

@@ -174,4 +174,5 @@ hipError_t launch_sum(const DevTables& T, const SumArgs& a, uint32_t* out, uint3
 hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
                          hipStream_t s);
 
+
 }  // namespace ckks

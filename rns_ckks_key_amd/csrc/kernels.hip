@@ -21,8 +21,8 @@
 // the key (k_ip: special primes, and the ciphertext primes together with the
 // end of ModDown) regenerate each tile once per workgroup and reuse it for
 // every ciphertext of the batch (Perseus summary on ai4snews, "Interpretation"
-// paragraph 2: the uniform key half is regenerated by counter-mode ChaCha12
-// inside the two kernels that use the key).  k_conv_mx is the conversion with its
+// paragraph 2: the random half of the key is rebuilt from a seed with ChaCha12
+// in counter mode by the kernels that consume the key).  k_conv_mx is the conversion with its
 // sums over sources as int8 matrix-core products (selected per context).  A
 // relinearisation never stores its tensor product: the inverse row pass forms
 // x1*y1 (k_row MUL) and the final inner-product pass the other products (TENSOR).
@@ -30,10 +30,6 @@
 
 #include "ckks_internal.h"
 #include "modarith.h"
-
-#ifndef IP1_WAVES
-#define IP1_WAVES 2
-#endif
 
 namespace ckks {
 
@@ -1096,9 +1092,11 @@ template <bool FINAL, bool TENSOR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_ip4(DevTables T, IpArgs a) {
   ip_body<FINAL, 4, TENSOR>(T, a);
 }
-// One wave per workgroup (hoisted keys, multi-item groups, small batches).
+// One wave per workgroup (hoisted keys, multi-item groups, small batches).  At
+// least two waves per SIMD: the register budget that keeps the single-wave shapes
+// fastest when every key is used once.
 template <bool FINAL, bool TENSOR = false>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(IP1_WAVES, 8))) void k_ip1(DevTables T, IpArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_ip1(DevTables T, IpArgs a) {
   ip_body<FINAL, 1, TENSOR>(T, a);
 }
 
@@ -1340,10 +1338,7 @@ hipError_t launch_col(const DevTables& T, const ColArgs& a, bool fwd, bool scale
              : col_dispatch<false>(T, a, scale_ninv ? 1u : 0u, items, s);
 }
 
-#ifndef CONV_CW
-#define CONV_CW 16
-#endif
-// Columns per workgroup.  A workgroup has 16 or 32 threads per column, 256 or 512
+// Columns per workgroup (16).  A workgroup has 16 or 32 threads per column, 256 or 512
 // threads.  256: 4 waves, and its 48 KB of LDS allows three per CU (12 waves).  512:
 // 8 waves, and registers (at most 128 per lane) allow two per CU (16 waves).  A
 // launch takes 512 when a workgroup has at least 512 (target, column) tasks, as the
@@ -1353,7 +1348,7 @@ hipError_t launch_col(const DevTables& T, const ColArgs& a, bool fwd, bool scale
 // and both conversions take 6-10% longer.  Fewer tasks keep 256 threads: 384 tasks on
 // 512 threads would leave a quarter of the lanes idle.  (12 threads per column were
 // slower, and 20 or 24 did not divide the tasks.)
-constexpr int kConvCW = CONV_CW;
+constexpr int kConvCW = 16;
 
 template <int LOGC, int MAXS>
 static void conv_go(const DevTables& T, const ConvArgs& a, dim3 grid, bool wide, hipStream_t s) {

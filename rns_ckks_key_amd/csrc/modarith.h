@@ -76,9 +76,6 @@ __host__ __device__ __forceinline__ uint32_t mont_mul(uint32_t a, uint32_t b, Mo
   return sub_mod(hi, t, md.q);
 }
 
-// Canonical residue of a 32-bit representative x.  For q > 2^31, x < 2q and one
-// conditional subtraction does it (min(x, x - q): x - q wraps above x when x < q);
-// otherwise x is multiplied by one = (2^32 mod q, companion), i.e. reduced by REDC.
 // a - b*c*2^-32 (mod q) for any 32-bit a and b and c < q, as a 32-bit representative
 // (a lazy value).  The Montgomery product's two reduction cases fold into the
 // subtraction's: with u = t - hi (hi - t is the unreduced product, in (-q, q)), the
@@ -108,6 +105,9 @@ __host__ __device__ __forceinline__ uint32_t lazy_add_mont(uint32_t a, uint32_t 
   return s + (neg ? md.q : 0u) + (carry ? nq : 0u);
 }
 
+// Canonical residue of a 32-bit representative x.  For q > 2^31, x < 2q and one
+// conditional subtraction does it (min(x, x - q): x - q wraps above x when x < q);
+// otherwise x is multiplied by one = (2^32 mod q, companion), i.e. reduced by REDC.
 __host__ __device__ __forceinline__ uint32_t canon(uint32_t x, uint32_t q, uint32_t one_wm, uint32_t one_wmq) {
   if (q >> 31) {
     const uint32_t d = x - q;

@@ -70,9 +70,10 @@ def test_host_context_validates_calls_before_any_launch():
     ctx = Context.for_chain(12, 4, 2, 2, 30, max_batch=0)
     h = ctx.handle
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call stops before launching
+    far = ctypes.c_void_p(0x1000000)  # 16 MiB on: clear of every [.][4..6][4096] range at `fake`
     seed = bytes(32)
 
-    def ks(ct=fake, level=4, kb=fake, sd=seed, ka=None, g=5, out=fake, batch=1):
+    def ks(ct=fake, level=4, kb=fake, sd=seed, ka=None, g=5, out=far, batch=1):
         return lib.ckks_keyswitch(h, ct, level, kb, sd, ka, g, out, batch, None)
 
     assert ks(level=0) == ERANGE
@@ -85,6 +86,26 @@ def test_host_context_validates_calls_before_any_launch():
     assert ks(out=None) == EINVAL
     assert ks(sd=None, ka=None) == EINVAL
     assert ks() == EINVAL and "host-only" in lib.ckks_last_error().decode()
+    # out may not overlap ct or either key half ([2][4][4096] and [2][6][4096] words)
+    words = 2 * 4 * 4096
+    assert ks(out=ctypes.c_void_p(0x1000 + 4 * (words - 1))) == EINVAL and "overlaps ct" in lib.ckks_last_error().decode()
+    hi = ctypes.c_void_p(0x200000)
+    assert ks(ct=hi, out=ctypes.c_void_p(0x200000 - 4 * (words - 1))) == EINVAL
+    assert "overlaps ct" in lib.ckks_last_error().decode()
+    assert ks(ct=far, kb=fake, out=ctypes.c_void_p(0x1000 + 4 * 8000)) == EINVAL
+    assert "overlaps key_b" in lib.ckks_last_error().decode()
+    assert ks(ct=far, kb=ctypes.c_void_p(0x2000000), ka=fake, out=ctypes.c_void_p(0x1000 + 4 * 8000)) == EINVAL
+    assert "overlaps key_a" in lib.ckks_last_error().decode()
+    assert ks(kb=ctypes.c_void_p(0x2000000), out=ctypes.c_void_p(0x1000 + 4 * words)) == EINVAL  # adjacent is fine
+    assert "host-only" in lib.ckks_last_error().decode()
+    assert lib.ckks_modup(h, fake, 4, ctypes.c_void_p(0x1000 + 4 * 4096), 1, None) == EINVAL
+    assert "overlaps" in lib.ckks_last_error().decode()
+    assert lib.ckks_modup(h, fake, 4, ctypes.c_void_p(0x1000 + 4 * 4 * 4096), 1, None) == EINVAL
+    assert "host-only" in lib.ckks_last_error().decode()
+    assert lib.ckks_moddown(h, fake, 4, ctypes.c_void_p(0x1000 + 4 * 5 * 4096), 1, None) == EINVAL
+    assert "overlaps x" in lib.ckks_last_error().decode()
+    assert lib.ckks_moddown(h, fake, 4, ctypes.c_void_p(0x1000 + 4 * 6 * 4096), 1, None) == EINVAL
+    assert "host-only" in lib.ckks_last_error().decode()
     assert lib.ckks_ntt_fwd(h, fake, 5, 2, 1, None) == ERANGE  # limbs 5..6 beyond 6 primes
     assert lib.ckks_ntt_fwd(h, None, 0, 2, 1, None) == EINVAL
     assert lib.ckks_ntt_inv(h, fake, 0, 0, 1, None) == ERANGE
@@ -96,10 +117,15 @@ def test_host_context_validates_calls_before_any_launch():
     assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, fake, None) == ERANGE
     gal = (U32 * 2)(5, 25)
     assert lib.ckks_keyswitch_hoisted(h, fake, 4, 0, kb, seed * 2, None, gal, fake, None) == ERANGE
-    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, None, None, gal, fake, None) == EINVAL
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, None, None, gal, far, None) == EINVAL
     assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, fake, None) == EINVAL
+    assert "overlaps ct" in lib.ckks_last_error().decode()
+    kb2 = (ctypes.c_void_p * 2)(0x2000000, 0x1000000 + 4 * 2 * 2 * 4 * 4096 - 4)  # key 1 meets out's last word
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb2, seed * 2, None, gal, far, None) == EINVAL
+    assert "overlaps key_b" in lib.ckks_last_error().decode()
+    assert lib.ckks_keyswitch_hoisted(h, fake, 4, 2, kb, seed * 2, None, gal, far, None) == EINVAL
+    assert "host-only" in lib.ckks_last_error().decode()
     assert lib.ckks_expand_a(h, None, fake, None) == EINVAL
-    far = ctypes.c_void_p(0x1000000)
     assert lib.ckks_rescale(h, fake, 1, far, 1, None) == ERANGE  # nothing to drop at level 1
     assert lib.ckks_rescale(h, fake, 5, far, 1, None) == ERANGE
     assert lib.ckks_rescale(h, None, 4, far, 1, None) == EINVAL
@@ -174,3 +200,4 @@ def test_conv_mfma_switch_validates_the_shape():
     assert lib.ckks_ctx_set_conv_mfma(wide.handle, 1) == EUNSUPPORTED
     wide.close()
     assert lib.ckks_ctx_set_conv_mfma(None, 1) == EINVAL
+
