@@ -8,7 +8,8 @@ import functools
 import numpy as np
 import pytest
 
-from tests.gpu_common import announce, context, first_mismatch, gpu, host, params, rand_limbs, torch
+from tests.gpu_common import CHAINS, announce, context, first_mismatch, gpu, host, params, rand_limbs, torch
+from oracle.pool import keyswitch_many
 
 pytestmark = pytest.mark.gpu
 
@@ -224,35 +225,53 @@ def test_multi_concurrent_sequences_share_a_small_workspace():
     assert all(same), [i for i, v in enumerate(same) if not v]
 
 
+@functools.lru_cache(maxsize=None)
+def _batch8_case():
+    """The batch-8, level-36, g = 5 case and the oracle's output for every ciphertext of it."""
+    pr = params("boot")
+    kb, ka, seed, s, s_src = oracle_key("boot", 5)
+    rng = np.random.default_rng(2)
+    ct = _ct(rng, pr, 36, 8)
+    want = np.stack(keyswitch_many(CHAINS["boot"], kb, ka, [(ct[b], 36, 5) for b in range(8)]))
+    return ct, want
+
+
 @pytest.mark.parametrize("variant", ["regen", "stored"])
-def test_keyswitch_boot_batch8_sampled(variant):
-    # the single key-switch workload: batch 8 at level 36, g = 5; ciphertexts 0 and 7 against the oracle
+def test_keyswitch_boot_batch8_every_ciphertext(variant):
+    # the single key-switch workload's launch shape: batch 8 at level 36, g = 5.  Every
+    # ciphertext (each is one wave of the eight-wave inner-product kernels) against the oracle.
     announce(f"keyswitch boot batch 8 {variant}")
     pr = params("boot")
     ctx = context("boot", 8)
     kb, ka, seed, s, s_src = oracle_key("boot", 5)
-    rng = np.random.default_rng(2)
-    ct = _ct(rng, pr, 36, 8)
+    ct, want = _batch8_case()
     out = ctx.keyswitch(gpu(ct), 36, gpu(kb), 5, key_seed=seed if variant == "regen" else None,
                         key_a=gpu(ka) if variant == "stored" else None)
     got = host(out)
-    for b in (0, 7):
-        want = oks.keyswitch(pr, ct[b], 36, kb, 5, key_a=ka)
-        assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
+    for b in range(8):
+        assert np.array_equal(got[b], want[b]), (b, first_mismatch(got[b], want[b]))
     assert oks.switch_error(pr, ct[3], got[3], 36, s, s_src, 5) < oks.noise_bound(pr, 36)
+
+
+@functools.lru_cache(maxsize=None)
+def _batch37_case():
+    pr = params("boot")
+    kb, ka, seed, s, s_src = oracle_key("boot", 25)
+    rng = np.random.default_rng(37)
+    ct = _ct(rng, pr, 36, 37)
+    want = keyswitch_many(CHAINS["boot"], kb, ka, [(ct[b], 36, 25) for b in (0, 17, 36)])
+    return ct, dict(zip((0, 17, 36), want))
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
 def test_keyswitch_boot_batch37_ragged(variant):
     # a batch of 37 at level 36 (each wave of the eight-wave kernels loops over four or
-    # five ciphertexts): ciphertexts 0 and 36 against the oracle (regenerated a-half),
-    # and the whole batch bit-identical to calls on slices of 8, 8, 8, 8 and 5
+    # five ciphertexts): ciphertexts 0, 17 and 36 against the oracle, and the whole
+    # batch bit-identical to calls on slices of 8, 8, 8, 8 and 5
     announce(f"keyswitch boot batch 37 {variant}")
-    pr = params("boot")
     ctx = context("boot", 37)
     kb, ka, seed, s, s_src = oracle_key("boot", 25)
-    rng = np.random.default_rng(37)
-    ct = _ct(rng, pr, 36, 37)
+    ct, want = _batch37_case()
     dct, dkb = gpu(ct), gpu(kb)
     kw = dict(key_seed=seed) if variant == "regen" else dict(key_a=gpu(ka))
     out = ctx.keyswitch(dct, 36, dkb, 25, **kw)
@@ -261,11 +280,9 @@ def test_keyswitch_boot_batch37_ragged(variant):
         if not torch.equal(part, out[lo:hi]):
             a, b = host(out[lo:hi]), host(part)
             pytest.fail(f"slice {lo}:{hi}: {first_mismatch(a, b)}")
-    if variant == "regen":
-        got = host(out)
-        for b in (0, 36):
-            want = oks.keyswitch(pr, ct[b], 36, kb, 25, key_a=ka)
-            assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
+    got = host(out)
+    for b, w in want.items():
+        assert np.array_equal(got[b], w), (b, first_mismatch(got[b], w))
 
 
 def test_keyswitch_boot_partial_digit_level():

@@ -6,16 +6,22 @@ b-halves are uniform residues (the same distribution as a real b-half): the bits
 of the output do not depend on whether the key is a valid encryption.
 """
 import functools
+import hashlib
+import json
+import os
 
 import numpy as np
 import pytest
 
-from tests.gpu_common import announce, context, first_mismatch, gpu, host, params
+from tests.gpu_common import CHAINS, announce, context, first_mismatch, gpu, host, params
+from oracle.pool import keyswitch_many
 
 pytestmark = pytest.mark.gpu
 
 from oracle import ks as oks  # noqa: E402
 from oracle.chacha import expand_key_a  # noqa: E402
+from oracle.ntt import intt, ntt, ntt_definition  # noqa: E402
+from oracle.params import Params  # noqa: E402
 from rns_ckks_key_amd import synth  # noqa: E402
 
 
@@ -31,38 +37,108 @@ def key_a(seed: bytes):
     return expand_key_a(seed, pr.primes, pr.dnum, pr.n)
 
 
-def test_level_sweep_batch16():
-    # workload 3: batch 16 at levels 36, 24, 12, 4 under workload 2's key
+SWEEP_SAMPLE = {36: 15, 24: 7, 12: 0, 4: 9}   # ciphertext of each level's batch checked against the oracle
+HOIST_SAMPLE = (0, 9, 15)                      # keys of the hoisted stage checked against the oracle
+
+
+@functools.lru_cache(maxsize=None)
+def _sweep_oracle():
+    pr = params("boot")
+    d = synth.draw(3, pr.primes)
+    seed = d.keys[0].seed
+    jobs = []
+    for li, level in enumerate(synth.WORKLOADS[3].levels):
+        jobs.append((d.cts[16 * li + SWEEP_SAMPLE[level]], level, 5))
+    want = keyswitch_many(CHAINS["boot"], key_rows(3003), key_a(seed), jobs)
+    return dict(zip(synth.WORKLOADS[3].levels, want))
+
+
+@pytest.mark.parametrize("variant", ["regen", "stored"])
+def test_level_sweep_batch16(variant):
+    # workload 3: batch 16 at levels 36, 24, 12, 4 under workload 2's key; one ciphertext per
+    # level against the oracle, with the a-half regenerated or stored
     pr = params("boot")
     ctx = context("boot", 16)
     d = synth.draw(3, pr.primes)
     seed = d.keys[0].seed
-    kb = key_rows(3003)
-    dkb = gpu(kb)
+    dkb = gpu(key_rows(3003))
+    dka = gpu(key_a(seed)) if variant == "stored" else None
+    want = _sweep_oracle()
     for li, level in enumerate(synth.WORKLOADS[3].levels):
-        announce(f"level sweep level={level}")
+        announce(f"level sweep level={level} {variant}")
         cts = np.stack(d.cts[16 * li:16 * li + 16])
-        got = host(ctx.keyswitch(gpu(cts), level, dkb, 5, key_seed=seed))
-        b = [15, 7, 0, 9][li]
-        want = oks.keyswitch(pr, cts[b].astype(np.uint64), level, kb, 5, key_a=key_a(seed))
-        assert np.array_equal(got[b], want), (level, b, first_mismatch(got[b], want))
+        got = host(ctx.keyswitch(gpu(cts), level, dkb, 5, key_seed=seed if dka is None else None, key_a=dka))
+        b = SWEEP_SAMPLE[level]
+        assert np.array_equal(got[b], want[level]), (level, b, first_mismatch(got[b], want[level]))
 
 
-def test_hoisted_sixteen_keys():
-    # workload 4: one ciphertext at level 36, 16 keys g = 5^k with their own seeds, one hoisted call
-    announce("hoisted 16 keys")
+@functools.lru_cache(maxsize=None)
+def _hoist_oracle():
+    pr = params("boot")
+    d = synth.draw(4, pr.primes)
+    kbs = [key_rows(4000 + k) for k in HOIST_SAMPLE]
+    kas = [key_a(d.keys[k].seed) for k in HOIST_SAMPLE]
+    jobs = [(d.cts[0], 36, d.keys[k].galois, i) for i, k in enumerate(HOIST_SAMPLE)]
+    return dict(zip(HOIST_SAMPLE, keyswitch_many(CHAINS["boot"], kbs, kas, jobs)))
+
+
+@pytest.mark.parametrize("variant", ["regen", "stored"])
+def test_hoisted_sixteen_keys(variant):
+    # workload 4: one ciphertext at level 36, 16 keys g = 5^k with their own seeds (or their
+    # stored a-halves), one hoisted call; three keys against the oracle
+    announce(f"hoisted 16 keys {variant}")
     pr = params("boot")
     ctx = context("boot", 16)
     d = synth.draw(4, pr.primes)
     ct = d.cts[0]
     keys = []
     for k, kd in enumerate(d.keys):
-        keys.append((gpu(key_rows(4000 + k)), kd.galois, kd.seed, None))
+        ka = gpu(key_a(kd.seed)) if variant == "stored" else None
+        keys.append((gpu(key_rows(4000 + k)), kd.galois, kd.seed if ka is None else None, ka))
     got = host(ctx.keyswitch_hoisted(gpu(ct), 36, keys))
-    for k in (0, 9, 15):
-        kd = d.keys[k]
-        want = oks.keyswitch(pr, ct.astype(np.uint64), 36, key_rows(4000 + k), kd.galois, key_a=key_a(kd.seed))
+    for k, want in _hoist_oracle().items():
         assert np.array_equal(got[k], want), (k, first_mismatch(got[k], want))
+
+
+@pytest.mark.parametrize("variant", ["regen", "stored"])
+def test_tiny_workload_exact_draw(variant):
+    # workload 1 exactly as drawn: N = 2^12, 4 + 2 primes below 2^30, dnum 2, the
+    # relinearisation-style key (s' -> s, g = 1) from the oracle's keygen on the drawn
+    # secrets, errors and seed; one key-switch, and the forward and inverse NTT of the
+    # ciphertext (every limb against the oracle, limb 0 also against the O(N^2) definition)
+    announce(f"workload 1 exact draw {variant}")
+    wl = synth.WORKLOADS[1]
+    pr = Params.make(wl.log_n, wl.L, wl.K, wl.dnum, wl.bits)
+    ctx = context("tiny", 1)
+    assert ctx.primes == pr.primes
+    d = synth.draw(1, pr.primes)
+    kd = d.keys[0]
+    kb, ka = oks.keygen(pr, d.s, d.s_prime, kd.errors, kd.seed)
+    ct = d.cts[0].astype(np.uint64)
+    got = host(ctx.keyswitch(gpu(ct[None]), 4, gpu(kb), 1, key_seed=kd.seed if variant == "regen" else None,
+                             key_a=gpu(ka) if variant == "stored" else None))[0]
+    want = oks.keyswitch(pr, ct, 4, kb, 1, seed=kd.seed)
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert oks.switch_error(pr, ct, got, 4, d.s, d.s_prime, 1) < oks.noise_bound(pr, 4)
+    # and the stored expected value (written from the oracle by tests/golden/make_golden.py)
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_golden.json")) as f:
+        golden = json.load(f)["workload1"]
+    assert hashlib.sha256(np.ascontiguousarray(got, dtype="<u4").tobytes()).hexdigest() == golden["sha256_keyswitch_out"]
+    # standalone NTT of the ciphertext [2][4][N]: its residues read as coefficients (a batch of
+    # two items of limbs q_0..q_3), forward then inverse in place, and the inverse on its own
+    qs, ps = pr.primes[:4], pr.psis[:4]
+    t = gpu(ct)
+    ctx.ntt_fwd(t, 0)
+    fwd = host(t)
+    want_f = ntt(ct, qs, ps)
+    assert np.array_equal(fwd, want_f), first_mismatch(fwd, want_f)
+    assert np.array_equal(fwd[0, 0], ntt_definition(ct[0, 0], qs[0], ps[0]))
+    ctx.ntt_inv(t, 0)
+    assert np.array_equal(host(t), ct)
+    t2 = gpu(ct)
+    ctx.ntt_inv(t2, 0)
+    want_i = intt(ct, qs, ps)
+    assert np.array_equal(host(t2), want_i), first_mismatch(host(t2), want_i)
 
 
 def test_mixed_stream_sixty_four():
@@ -80,12 +156,13 @@ def test_mixed_stream_sixty_four():
             dkb[k] = gpu(key_rows(5000 + k))
         lvl = d.levels[i]
         outs.append(ctx.keyswitch(gpu(ct[None]), lvl, dkb[k], wl.galois[k], key_seed=d.keys[k].seed))
-    for i in (0, 31, 63):
-        k, lvl = d.key_index[i], d.levels[i]
+    sample = (0, 31, 63)
+    ks = sorted({d.key_index[i] for i in sample})
+    jobs = [(d.cts[i], d.levels[i], wl.galois[d.key_index[i]], ks.index(d.key_index[i])) for i in sample]
+    wants = keyswitch_many(CHAINS["boot"], [key_rows(5000 + k) for k in ks], [key_a(d.keys[k].seed) for k in ks], jobs)
+    for i, want in zip(sample, wants):
         got = host(outs[i])[0]
-        want = oks.keyswitch(pr, d.cts[i].astype(np.uint64), lvl, key_rows(5000 + k), wl.galois[k],
-                             key_a=key_a(d.keys[k].seed))
-        assert np.array_equal(got, want), (i, lvl, k, first_mismatch(got, want))
+        assert np.array_equal(got, want), (i, d.levels[i], d.key_index[i], first_mismatch(got, want))
 
 
 def test_multi_item_equals_single_calls():
@@ -112,8 +189,9 @@ def test_multi_item_equals_single_calls():
         single = ctx.keyswitch(ct[None], lvl, kb, g, key_seed=seed, key_a=ka)
         a, b = host(outs[i]), host(single)[0]
         assert np.array_equal(a, b), (i, lvl, first_mismatch(a, b))
-    for i in (5, 40):
-        k, lvl = d.key_index[i], d.levels[i]
-        want = oks.keyswitch(pr, d.cts[i].astype(np.uint64), lvl, key_rows(5000 + k), wl.galois[k],
-                             key_a=key_a(d.keys[k].seed))
+    sample = (5, 40)
+    ks = sorted({d.key_index[i] for i in sample})
+    jobs = [(d.cts[i], d.levels[i], wl.galois[d.key_index[i]], ks.index(d.key_index[i])) for i in sample]
+    wants = keyswitch_many(CHAINS["boot"], [key_rows(5000 + k) for k in ks], [key_a(d.keys[k].seed) for k in ks], jobs)
+    for i, want in zip(sample, wants):
         assert np.array_equal(host(outs[i]), want), (i, first_mismatch(host(outs[i]), want))

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle.chain import chain_primes, min_root
-from oracle.ntt import intt, ntt
+from oracle.ntt import intt, ntt, ntt_definition
 from tests.bigint_helpers import brv, horner_eval, negacyclic_mul
 
 
@@ -80,3 +80,28 @@ def test_ntt_special_inputs():
     rng = np.random.default_rng(0)
     x = np.stack([np.stack([rng.integers(0, q, n, dtype=np.uint64) for q in qs]) for _ in range(3)])
     assert np.array_equal(ntt(x, qs, psis)[1], ntt(x[1], qs, psis))
+
+
+@pytest.mark.parametrize("n,bits", [(16, 20), (64, 32), (128, 30)])
+def test_ntt_definition_matches_horner_every_index(n, bits):
+    # the O(N^2) definition (a table of powers of psi) against Horner evaluation in Python integers
+    qs, psis = _setup(n, bits, 2)
+    rng = np.random.default_rng(n)
+    logn = n.bit_length() - 1
+    for q, psi in zip(qs, psis):
+        a = rng.integers(0, q, n, dtype=np.uint64)
+        a[-1] = q - 1
+        out = ntt_definition(a, q, psi)
+        for j in range(n):
+            assert int(out[j]) == horner_eval(a, pow(psi, 2 * brv(j, logn) + 1, q), q)
+
+
+@pytest.mark.parametrize("n,bits,count", [(16, 32, 3), (256, 30, 2), (1024, 32, 2), (4096, 30, 1)])
+def test_fast_ntt_equals_definition_every_index(n, bits, count):
+    # merged-twist Cooley-Tukey reaches the definition's values, every index, up to N = 2^12
+    qs, psis = _setup(n, bits, count)
+    rng = np.random.default_rng(n + count)
+    a = np.stack([rng.integers(0, q, n, dtype=np.uint64) for q in qs])
+    fast = ntt(a, qs, psis)
+    for i, (q, psi) in enumerate(zip(qs, psis)):
+        assert np.array_equal(fast[i], ntt_definition(a[i], q, psi)), i
