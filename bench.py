@@ -7,19 +7,29 @@ Inputs are synthetic and seeded (rns_ckks_key_amd.synth, workload 2), resident
 in HBM before timing; R copies of the ciphertexts and keys are rotated so that
 repeated steps cannot be served from the 256 MB Infinity Cache.
 
-Output: one JSON line (rank 0).  Besides the headline (regenerated a-half) it
-carries the stored-key variant, limb-NTTs/s, the roofline of the dominant
-kernel (algorithmic work per launch over its event-timed duration) and the CPU
-oracle timed on a bounded sample of the same workload.
+Timing.  Before anything is timed, both key variants run alternately for a fixed
+wall time (--prewarm seconds, whatever --warmup says), so the GPU's clocks have
+settled for both; then --warmup calls of each.  The headline is exactly --steps
+calls of the regenerated variant, bracketed by device synchronisations and HIP
+events on the stream the library launches on, with an event between calls.
+Then --rounds more blocks of --steps calls of each variant alternate (the order
+flips every round); the per-call samples of all blocks give the median, p10 and
+p90 of each variant.  Per-kernel times come from the library's per-launch event
+timer in separate, also alternating, blocks.
+
+Output: one JSON line.  Besides the headline it carries the stored-key variant,
+limb-NTTs/s (ring 2^16 batch and the 2^12 ciphertext), workloads 3-5 in both
+variants (unless --no-extra), the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample of the same workload (unless --no-cpu).
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -30,15 +40,18 @@ LOG_N, L, K, DNUM, BITS = 16, 36, 12, 3, 32
 N = 1 << LOG_N
 BATCH, LEVEL, GALOIS = 8, 36, 5
 SMALL_RING = (15, 20, 7, 3)           # log N, ciphertext primes, special primes, dnum of the smaller-ring workload
+TINY = (12, 4, 2, 2, 30)              # log N, L, K, dnum, bits of the small workload
 ROTATE = 4
 
 # ---------------------------------------------------------------- work model
-# Algorithmic work in 32-bit VALU lane-op slots (one full-rate op on one lane),
-# with gfx950's measured full-rate 32-bit multiplies: a butterfly is one
-# Montgomery constant multiply (3 multiplies + 3 adds) plus a modular add and a
-# modular subtract; a MAC is a 32x32->64 product accumulated into 96 bits; a
-# reduction is the two-word REDC; ChaCha12 is 12 rounds x 4 quarter rounds x 12
-# ops / 16 words + feed-forward and rejection.
+# Algorithmic work in 32-bit VALU lane-op slots (one full-rate op on one lane):
+# the per-unit costs of the survey's model with full-rate 32-bit multiplies
+# (measured on gfx950): a butterfly is one Montgomery constant multiply (3
+# multiplies + 3 adds) plus a modular add and a modular subtract; a MAC is a
+# 32x32->64 product accumulated into 96 bits; a reduction is the two-word REDC;
+# ChaCha12 is 12 rounds x 4 quarter rounds x 12 ops / 16 words + feed-forward and
+# rejection.  These count the method's work, not the compiled instructions (the
+# counter table under profiles/ gives those).
 SLOT = {"bfly": 13, "cmul": 6, "mac": 5, "red": 9, "chacha_word": 42}
 VALU_PEAK = 256 * 4 * 16 * 2.4e9      # lane-op slots/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 HBM_PEAK = 8.0e12                      # bytes/s
@@ -87,7 +100,7 @@ def hbm_bytes(level: int, batch: int, regen: bool, n_keys: int = 1) -> float:
     return ct + out + n_keys * key_rows * (1 if regen else 2)
 
 
-# ---------------------------------------------------------------- helpers
+# ---------------------------------------------------------------- committed counter summaries
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -97,61 +110,186 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str) -> dict | None:
-    """Per-launch HBM bytes of `kernel` from the committed rocprofv3 counter summary, if still current."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_keyswitch_batch8_l36.md")
+def _current_profile(name: str) -> str | None:
+    """Text of profiles/<name> if its kernel-source-hash matches the sources (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel-source-hash:\s*([0-9a-f]+)", text)
-    if not m or m.group(1) != kernel_source_hash():
-        return None
-    m = re.search(rf"^\|\s*{kernel}\s*\|\s*([0-9.e+]+)\s*\|\s*([0-9.e+]+)\s*\|", text, re.M)
+    return text if m and m.group(1) == kernel_source_hash() else None
+
+
+def read_traffic(kernel: str) -> dict | None:
+    """Per-launch HBM bytes of `kernel` from the committed rocprofv3 counter summary, if still current."""
+    text = _current_profile("hbm_traffic_keyswitch_batch8_l36.md")
+    m = text and re.search(rf"^\|\s*{kernel}\s*\|\s*([0-9.e+]+)\s*\|\s*([0-9.e+]+)\s*\|", text, re.M)
+    return {"fetch_bytes": float(m.group(1)), "write_bytes": float(m.group(2))} if m else None
+
+
+def read_issue(kernel: str) -> dict | None:
+    """VALU instructions and issue fraction of `kernel` from the committed SQ counter summary, if current."""
+    text = _current_profile("valu_issue_keyswitch_batch8_l36.md")
+    m = text and re.search(rf"^\|\s*{kernel}\s*\|\s*([0-9.e+]+)\s*\|\s*([0-9.e+]+)\s*\|\s*([0-9.]+)\s*\|"
+                           rf"\s*([0-9.]+)\s*\|", text, re.M)
     if not m:
         return None
-    return {"fetch_bytes": float(m.group(1)), "write_bytes": float(m.group(2))}
+    return {"valu_insts": float(m.group(1)), "cycles": float(m.group(2)), "cycles_per_valu_inst": float(m.group(3)),
+            "issue_frac": float(m.group(4))}
 
 
-def time_calls(fn, steps: int, warmup: int, torch) -> float:
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+def read_valu_rates() -> dict | None:
+    """Measured lane-op rates (T/s) of gfx950 integer instructions from the committed microbenchmark summary."""
+    path = os.path.join(ROOT, "profiles", "valu_rates_gfx950.md")
+    if not os.path.exists(path):
+        return None
+    rates = {}
+    for m in re.finditer(r"^\|\s*(v_[a-z0-9_]+)\s*\|\s*([0-9.]+)\s*\|", open(path).read(), re.M):
+        rates[m.group(1)] = float(m.group(2))
+    return rates or None
+
+
+# ---------------------------------------------------------------- timing
+
+def timed_block(fn, steps: int, torch) -> list[float]:
+    """Exactly `steps` calls on torch's current stream (the library launches there), bracketed by
+    device synchronisations; returns the per-call ms from events recorded between calls."""
     s = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(s)
     for i in range(steps):
         fn(i)
-    e1.record(s)
+        ev[i + 1].record(s)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms per call
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
-def cpu_baseline(primes, draw, budget_s: float) -> dict:
-    """The oracle as it stands, on host cores, on ciphertexts of the same workload."""
+def prewarm(fns: list, seconds: float, torch) -> float:
+    """Runs the calls alternately for at least `seconds` of wall time; returns the time spent."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for fn in fns:
+            fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return time.perf_counter() - t0
+
+
+def stats(samples: list[float], blocks: list[float], items: float, unit: str) -> dict:
+    q = statistics.quantiles(samples, n=10, method="inclusive") if len(samples) > 1 else samples * 9
+    mean = sum(samples) / len(samples)
+    return {unit: round(items / (mean * 1e-3), 1), "ms_per_call": round(mean, 4),
+            "ms_median": round(statistics.median(samples), 4), "ms_p10": round(q[0], 4), "ms_p90": round(q[-1], 4),
+            f"{unit}_at_median": round(items / (statistics.median(samples) * 1e-3), 1),
+            "block_means_ms": [round(b, 4) for b in blocks], "calls_timed": len(samples)}
+
+
+def interleaved(fns: dict, steps: int, warmup: int, rounds: int, torch, ctx=None, items: float = 1,
+                unit: str = "per_s", first: dict | None = None) -> dict:
+    """Warm-up, then `rounds` alternating blocks of `steps` calls of each variant (order flipped every
+    round), then two alternating profiled blocks each for per-kernel times.  `first` holds per-call
+    samples already timed for a variant (the headline block)."""
+    for fn in fns.values():
+        for i in range(warmup):
+            fn(i)
+    names = list(fns)
+    samples = {k: list((first or {}).get(k, [])) for k in names}
+    blocks = {k: ([sum(samples[k]) / len(samples[k])] if samples[k] else []) for k in names}
+    for r in range(rounds):
+        for k in (names if r % 2 == 0 else names[::-1]):
+            t = timed_block(fns[k], steps, torch)
+            samples[k] += t
+            blocks[k].append(sum(t) / steps)
+    out = {k: stats(samples[k], blocks[k], items, unit) for k in names}
+    if ctx is not None:
+        acc = {k: {} for k in names}
+        for r in range(2):
+            for k in (names if r % 2 == 0 else names[::-1]):
+                ctx.profile(True)
+                for i in range(steps):
+                    fns[k](i)
+                ctx.profile(False)
+                for c, (ms, n) in ctx.profile_read().items():
+                    if n:
+                        a = acc[k].setdefault(c, [0.0, 0])
+                        a[0] += ms
+                        a[1] += n
+        for k in names:
+            out[k]["kernel_ms_per_call"] = {c: round(v[0] / (2 * steps), 4) for c, v in acc[k].items()}
+            out[k]["kernel_ms_per_launch"] = {c: round(v[0] / v[1], 4) for c, v in acc[k].items()}
+    return out
+
+
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+
+def host_cpu() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import numpy as np
+    return {"cpu_model": model, "available_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+
+
+def cpu_baseline(primes, cts, key_b, seed: bytes) -> dict:
+    """The oracle as it stands, on the host's cores, on ciphertexts of the headline workload.
+
+    One core: one regenerated-key and one stored-key switch at level 36, and the forward and
+    inverse transform of 36 limbs.  All cores: one stored-key switch per worker process at once."""
     import numpy as np
 
-    from oracle import ks as oks
+    from oracle import ks as oks, pool
+    from oracle.chacha import expand_key_a
+    from oracle.ntt import intt, ntt
     from oracle.params import Params
 
     pr = Params.make(LOG_N, L, K, DNUM, BITS)
     assert pr.primes == list(primes), "library and oracle chains differ"
-    key_b = np.asarray(draw["key_b"], dtype=np.uint64)
-    done, t0 = 0, time.perf_counter()
-    for b in range(BATCH):
-        ct = draw["cts"][b].astype(np.uint64)
-        oks.keyswitch(pr, ct, LEVEL, key_b, GALOIS, seed=draw["seed"])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "key-switches/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of the 8 ciphertexts at level 36, g=5, a-half regenerated from the seed "
-                      f"(numpy, single-threaded elementwise); {dt:.1f} s on {len(os.sched_getaffinity(0))} "
-                      f"available host cores"}
+    kb = np.asarray(key_b, dtype=np.uint64)
+    ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
+    t0 = time.perf_counter()
+    oks.keyswitch(pr, cts[0].astype(np.uint64), LEVEL, kb, GALOIS, seed=seed)
+    t_regen = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oks.keyswitch(pr, cts[1].astype(np.uint64), LEVEL, kb, GALOIS, key_a=ka)
+    t_stored = time.perf_counter() - t0
+    x = cts[2][0].astype(np.uint64)
+    t0 = time.perf_counter()
+    y = ntt(x, pr.primes[:LEVEL], pr.psis[:LEVEL])
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    intt(y, pr.primes[:LEVEL], pr.psis[:LEVEL])
+    t_inv = time.perf_counter() - t0
+    n_w = pool.workers(16)
+    ex = pool.start_pool((LOG_N, L, K, DNUM, BITS), kb, ka, n_w)
+    try:
+        jobs = [(cts[i % len(cts)], LEVEL, GALOIS) for i in range(n_w)]
+        t0 = time.perf_counter()
+        pool.run_jobs(ex, jobs)
+        t_all = time.perf_counter() - t0
+    finally:
+        ex.shutdown()
+    return {"value": round(n_w / t_all, 4), "unit": "key-switches/s", "cores": n_w, "kind": "oracle",
+            "sample": f"{n_w} ciphertexts of the batch-8, level-36, g=5 workload, one per worker process "
+                      f"(stored a-half), switched at once on {n_w} cores in {t_all:.1f} s; one core: one "
+                      f"regenerated ({t_regen:.1f} s) and one stored ({t_stored:.1f} s) switch, and the "
+                      f"forward and inverse NTT of 36 limbs",
+            "single_core": {"regen_key_switches_per_s": round(1 / t_regen, 4),
+                            "stored_key_switches_per_s": round(1 / t_stored, 4),
+                            "ntt_limbs_per_s": {"forward": round(LEVEL / t_fwd, 1), "inverse": round(LEVEL / t_inv, 1)}},
+            "host": host_cpu()}
 
 
-# ---------------------------------------------------------------- main
+# ---------------------------------------------------------------- headline
 
 def make_context(primes, max_batch: int, args):
     from rns_ckks_key_amd.api import Context
@@ -160,49 +298,12 @@ def make_context(primes, max_batch: int, args):
     return ctx
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--conv", choices=["vector", "matrix"], default="vector",
-                    help="base conversion on the vector unit or the matrix cores")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7, 8], default=2,
-                    help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
-                         "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36; "
-                         "7: 4 x 4 baby-step/giant-step linear transform at level 36; "
-                         "8: smaller ring N=2^15 (20+7 primes, dnum 3), batch 8 at level 20")
-    ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
-                    help="which key variants to time (the headline is always the regenerated one when timed)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 512 MiB device copy (xor with 0) three times, to calibrate HBM counters")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: key-switching is not sharded across GPUs in this library "
-              "(see the design notes); run with --gpus 1", file=sys.stderr)
-        return 2
-
+def headline(args, primes, torch):
     import numpy as np
-    import torch
-
-    if args.copy_calibration:
-        src = torch.randint(0, 2**31 - 1, (128 << 20,), dtype=torch.int32, device="cuda")  # 512 MiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.bitwise_xor(src, 0, out=dst)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 3}))
-        return 0
 
     from rns_ckks_key_amd import synth
-    from rns_ckks_key_amd.api import Context, chain_primes, to_device
+    from rns_ckks_key_amd.api import to_device
 
-    torch.cuda.set_device(0)
-    if args.workload != 2:
-        return other_workload(args)
-    primes = chain_primes(LOG_N, BITS, L + K)
     ctx = make_context(primes, BATCH, args)
     d = synth.draw(2, primes)
     seed = d.keys[0].seed
@@ -222,44 +323,61 @@ def main() -> int:
         ctx.keyswitch(dev_ct[r], LEVEL, dev_kb[r], GALOIS, key_seed=seed if regen else None,
                       key_a=None if regen else dev_ka[r], out=outs[r])
 
-    res = {}
-    variants = [v for v in (("regen", True), ("stored", False)) if args.variant in ("both", v[0])]
-    for variant, regen in variants:
-        ms = time_calls(lambda i: step(i, regen), args.steps, args.warmup, torch)
-        ctx.profile(True)
-        for i in range(args.steps):
-            step(i, regen)
-        ctx.profile(False)
-        prof = ctx.profile_read()
-        res[variant] = {"ms_per_step": ms, "key_switches_per_s": BATCH / (ms * 1e-3), "prof": prof}
-        print(f"[bench] {variant}: {ms:.3f} ms per batch of {BATCH}", file=sys.stderr, flush=True)
+    fns = {v: (lambda i, rg=(v == "regen"): step(i, rg)) for v in ("regen", "stored")
+           if args.variant in ("both", v)}
+    head_name = "regen" if "regen" in fns else "stored"
+    warmed = prewarm(list(fns.values()), args.prewarm, torch)
+    for fn in fns.values():
+        for i in range(args.warmup):
+            fn(i)
+    # the headline: exactly --steps calls of one variant
+    head_samples = timed_block(fns[head_name], args.steps, torch)
+    head_ms = sum(head_samples) / args.steps
+    res = interleaved(fns, args.steps, 0, args.rounds, torch, ctx=ctx, items=BATCH, unit="key_switches_per_s",
+                      first={head_name: head_samples})
+    for v in res:
+        print(f"[bench] {v}: median {res[v]['ms_median']:.4f} ms per batch of {BATCH}", file=sys.stderr, flush=True)
 
-    # limb-NTTs/s on [8][72][N]
-    x = torch.randint(0, 2**31 - 1, (BATCH, 2 * LEVEL, N), dtype=torch.int32, device="cuda")
-    xr = x.view(BATCH * 2, LEVEL, N)
-    ms_f = time_calls(lambda i: ctx.ntt_fwd(xr, 0), args.steps, args.warmup, torch)
-    ms_i = time_calls(lambda i: ctx.ntt_inv(xr, 0), args.steps, args.warmup, torch)
-    limbs = BATCH * 2 * LEVEL
+    # limb-NTTs/s on [16][36][N], and on the small workload's ciphertext [2][4][2^12]
+    x = torch.randint(0, 2**31 - 1, (BATCH * 2, LEVEL, N), dtype=torch.int32, device="cuda")
+    nt = interleaved({"forward": lambda i: ctx.ntt_fwd(x, 0), "inverse": lambda i: ctx.ntt_inv(x, 0)},
+                     args.steps, args.warmup, 2, torch, items=BATCH * 2 * LEVEL, unit="limb_ntts_per_s")
+    from rns_ckks_key_amd.api import Context
+    tiny = Context(TINY[0], TINY[1], TINY[2], TINY[3], synth_chain(TINY), max_batch=1)
+    y = torch.randint(0, 2**29, (2, TINY[1], 1 << TINY[0]), dtype=torch.int32, device="cuda")
+    nt1 = interleaved({"forward": lambda i: tiny.ntt_fwd(y, 0), "inverse": lambda i: tiny.ntt_inv(y, 0)},
+                      args.steps, args.warmup, 2, torch, items=2 * TINY[1], unit="limb_ntts_per_s")
+    tiny.close()
 
-    head_name = "regen" if "regen" in res else "stored"
     head = res[head_name]
     wm = work_model(LEVEL, BATCH, head_name == "regen")
-    prof = head["prof"]
-    per_launch = {k: prof[k][0] / prof[k][1] for k in prof if prof[k][1]}
-    dominant = max(per_launch, key=lambda k: prof[k][0])
+    per_launch = head["kernel_ms_per_launch"]
+    per_call = head["kernel_ms_per_call"]
+    dominant = max(per_call, key=per_call.get)
     t_dom = per_launch[dominant] * 1e-3
     achieved = wm[dominant] / t_dom
     traffic = read_traffic(dominant)
+    issue = read_issue(dominant)
+    rates = read_valu_rates()
     total_slots = sum(wm.values())
-    t_call = head["ms_per_step"] * 1e-3
+    t_call = head_ms * 1e-3
+    roof = {"bound": "alu", "kernel": dominant, "achieved": round(achieved / 1e12, 3),
+            "peak": round(VALU_PEAK / 1e12, 3), "unit": "T lane-op slots/s", "frac": round(achieved / VALU_PEAK, 4),
+            "work_per_launch_slots": wm[dominant], "avg_launch_ms": round(per_launch[dominant], 4),
+            "traffic": None if traffic is None else traffic["fetch_bytes"] + traffic["write_bytes"],
+            "counters": issue}
+    if rates and "v_add_u32" in rates:
+        # the same work priced at the measured rate of the cheapest (add-class) instruction: a lower bound
+        roof["frac_vs_add_rate"] = round(achieved / (rates["v_add_u32"] * 1e12), 4)
+        roof["add_rate_T_per_s"] = rates["v_add_u32"]
     out = {
         "metric": "key-switches/sec at N=2^16, 36+12 x 32-bit primes; % of HBM roofline",
-        "value": round(head["key_switches_per_s"], 1),
+        "value": round(BATCH / t_call, 1),
         "unit": "key-switches/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms_per_step"], 4),
+        "ms_per_step": round(head_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -268,100 +386,117 @@ def main() -> int:
         "config": {"workload": "single key-switch at bootstrapping scale: batch 8 ciphertexts, level 36, "
                                "one rotation key g=5, a-half regenerated in-kernel by ChaCha12",
                    "N": N, "L": L, "K": K, "dnum": DNUM, "batch": BATCH, "level": LEVEL, "galois": GALOIS,
-                   "variant": "regen", "input_copies_rotated": ROTATE},
-        "roofline": {"bound": "alu", "kernel": dominant, "achieved": round(achieved / 1e12, 3),
-                     "peak": round(VALU_PEAK / 1e12, 3), "unit": "T lane-op slots/s",
-                     "frac": round(achieved / VALU_PEAK, 4),
-                     "work_per_launch_slots": wm[dominant], "avg_launch_ms": round(per_launch[dominant], 4),
-                     "traffic": None if traffic is None else traffic["fetch_bytes"] + traffic["write_bytes"]},
+                   "variant": head_name, "input_copies_rotated": ROTATE,
+                   "conversion": "matrix cores (int8 MFMA)" if args.conv == "matrix" else "vector unit"},
+        "timing": {"prewarm_s": round(warmed, 2), "prewarm": "both variants alternately before any timing",
+                   "headline_block": "exactly `steps` calls after the pre-warm and `warmup` calls of each variant",
+                   "interleaved_rounds": args.rounds},
+        "roofline": roof,
         "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, head_name == "regen") / t_call / HBM_PEAK, 4),
         "valu_frac_whole_call": round(total_slots / t_call / VALU_PEAK, 4),
-        "kernel_ms_per_call": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]},
-        "ntt_limbs_per_s": {"forward": round(limbs / (ms_f * 1e-3)), "inverse": round(limbs / (ms_i * 1e-3)),
-                            "shape": [BATCH * 2, LEVEL, N]},
+        "variants": res,
+        "ntt_limbs_per_s": {"ring_2^16_batch": {"shape": [BATCH * 2, LEVEL, N], **nt},
+                            "ring_2^12_one_ciphertext": {"shape": [2, TINY[1], 1 << TINY[0]], **nt1}},
+        "key_bytes": {"stored": 2 * DNUM * (L + K) * N * 4, "regen": DNUM * (L + K) * N * 4 + 32},
     }
-    out["config"]["variant"] = head_name
-    out["config"]["conversion"] = "matrix cores (int8 MFMA)" if args.conv == "matrix" else "vector unit"
-    if "stored" in res and head_name != "stored":
-        st = res["stored"]
-        sp = st["prof"]
-        out["stored_key"] = {"value": round(st["key_switches_per_s"], 1), "ms_per_step": round(st["ms_per_step"], 4),
-                             "hbm_roofline_frac": round(hbm_bytes(LEVEL, BATCH, False) / (st["ms_per_step"] * 1e-3)
-                                                        / HBM_PEAK, 4),
-                             "kernel_ms_per_call": {k: round(sp[k][0] / args.steps, 4) for k in sp if sp[k][1]}}
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(primes, {"cts": cts, "key_b": kb_host, "seed": seed}, args.cpu_budget)
-    print(json.dumps(out))
     ctx.close()
-    return 0
+    return out, {"cts": cts, "key_b": kb_host, "seed": seed}
 
 
-def other_workload(args) -> int:
-    """Workloads 3-8: one JSON line each (not the headline); kernel times from the event timer."""
+def synth_chain(t) -> list[int]:
+    from rns_ckks_key_amd.api import chain_primes
+    return chain_primes(t[0], t[4], t[1] + t[2])
+
+
+# ---------------------------------------------------------------- other workloads
+
+def run_workload(w: int, args, primes, torch) -> dict:
+    """Workloads 3-8 in the requested variants; kernel times from the event timer."""
     import numpy as np
-    import torch
 
     from rns_ckks_key_amd import synth
     from rns_ckks_key_amd.api import Context, chain_primes, to_device
 
-    primes = chain_primes(LOG_N, BITS, L + K)
     variants = [v for v in ("regen", "stored") if args.variant in ("both", v)]
-    if args.workload == 6:
-        name, unit = "multiply + relinearise (s^2 key) + rescale, N=2^16, batch 8 at level 36 -> 35", "products/s"
-    elif args.workload == 7:
-        name, unit = ("double-hoisted baby-step/giant-step linear transform, N=2^16, level 36, n1 = n2 = 4 "
-                      "(16 diagonals, 3 baby + 3 giant rotation keys g = 5^k)", "transforms/s")
-    elif args.workload == 8:
-        name, unit = ("smaller ring: N=2^15, 20+7 x 32-bit primes, dnum 3, batch 8 ciphertexts at level 20, "
-                      "one rotation key g=5", "key-switches/s")
+    steps, warmup, rounds = args.steps, args.warmup, max(1, args.rounds // 2)
+
+    def both(make_fn, items, unit, ctx):
+        return interleaved({v: make_fn(v) for v in variants}, steps, warmup, rounds, torch, ctx=ctx, items=items,
+                           unit=unit)
+
+    if w == 6:
+        name = "multiply + relinearise (s^2 key) + rescale, N=2^16, batch 8 at level 36 -> 35"
+    elif w == 7:
+        name = ("double-hoisted baby-step/giant-step linear transform, N=2^16, level 36, n1 = n2 = 4 "
+                "(16 diagonals, 3 baby + 3 giant rotation keys g = 5^k)")
+    elif w == 8:
+        name = "smaller ring: N=2^15, 20+7 x 32-bit primes, dnum 3, batch 8 ciphertexts at level 20, one rotation key g=5"
     else:
-        wl = synth.WORKLOADS[args.workload]
-        d = synth.draw(args.workload, primes)
-        name, unit = wl.name, "key-switches/s"
-    res = {"metric": f"workload {args.workload}: {name}", "unit": unit, "n_gpus": 1,
-           "dtype": "u32", "data": "synthetic", "steps": args.steps, "warmup": args.warmup}
-    if args.workload == 3:
+        wl = synth.WORKLOADS[w]
+        d = synth.draw(w, primes)
+        name = wl.name
+    res = {"metric": f"workload {w}: {name}", "n_gpus": 1, "dtype": "u32", "data": "synthetic", "steps": steps,
+           "warmup": warmup, "rounds": rounds}
+    if w == 3:
         ctx = make_context(primes, 16, args)
         kb = to_device(synth.uniform_key_rows(3003, primes, DNUM, N))
         seed = d.keys[0].seed
         ka = ctx.expand_a(seed)
-        per = {}
+        res["levels"] = {}
         for li, level in enumerate(wl.levels):
             cts = to_device(np.stack(d.cts[16 * li:16 * li + 16]))
             out = torch.empty((16, 2, level, N), dtype=torch.int32, device="cuda")
-            for v in variants:
-                fn = (lambda i, lv=level, c=cts, o=out, v=v: ctx.keyswitch(c, lv, kb, 5, key_seed=seed if v == "regen"
-                                                                           else None, key_a=ka if v == "stored"
-                                                                           else None, out=o))
-                ms = time_calls(fn, args.steps, args.warmup, torch)
-                ctx.profile(True)
-                for i in range(args.steps):
-                    fn(i)
-                ctx.profile(False)
-                prof = ctx.profile_read()
-                per[f"l{level}_{v}"] = {"key_switches_per_s": round(16 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-                                        "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-        res["levels"] = per
-    elif args.workload == 4:
+            mk = (lambda v, lv=level, c=cts, o=out: lambda i: ctx.keyswitch(
+                c, lv, kb, 5, key_seed=seed if v == "regen" else None, key_a=ka if v == "stored" else None, out=o))
+            r = both(mk, 16, "key_switches_per_s", ctx)
+            for v in r:
+                r[v]["hbm_roofline_frac"] = round(hbm_bytes(level, 16, v == "regen") / (r[v]["ms_per_call"] * 1e-3)
+                                                  / HBM_PEAK, 4)
+            res["levels"][str(level)] = r
+    elif w == 4:
         ctx = make_context(primes, 16, args)
         ct = to_device(d.cts[0])
         kbs = [to_device(synth.uniform_key_rows(4000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
         kas = [ctx.expand_a(kd.seed) for kd in d.keys]
         out = torch.empty((16, 2, LEVEL, N), dtype=torch.int32, device="cuda")
-        for v in variants:
+
+        def mk(v):
             keys = [(kbs[k], kd.galois, kd.seed if v == "regen" else None, kas[k] if v == "stored" else None)
                     for k, kd in enumerate(d.keys)]
-            fn = lambda i, keys=keys: ctx.keyswitch_hoisted(ct, LEVEL, keys, out=out)
-            ms = time_calls(fn, args.steps, args.warmup, torch)
-            ctx.profile(True)
-            for i in range(args.steps):
-                fn(i)
-            ctx.profile(False)
-            prof = ctx.profile_read()
-            res[v] = {"key_switches_per_s": round(16 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-                      "hbm_roofline_frac": round(hbm_bytes(LEVEL, 1, v == "regen", 16) / (ms * 1e-3) / HBM_PEAK, 4),
-                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-    elif args.workload == 6:
+            return lambda i: ctx.keyswitch_hoisted(ct, LEVEL, keys, out=out)
+        res.update(both(mk, 16, "key_switches_per_s", ctx))
+        for v in variants:
+            res[v]["hbm_roofline_frac"] = round(hbm_bytes(LEVEL, 1, v == "regen", 16) / (res[v]["ms_per_call"] * 1e-3)
+                                                / HBM_PEAK, 4)
+    elif w == 5:
+        ctx = make_context(primes, 16, args)
+        kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
+        kas = [ctx.expand_a(kd.seed) for kd in d.keys] if "stored" in variants else None
+        cts = [to_device(c) for c in d.cts]
+        outs = [torch.empty((2, lv, N), dtype=torch.int32, device="cuda") for lv in d.levels]
+
+        def items_of(v):
+            return [(cts[c], d.levels[c], kbs[d.key_index[c]], wl.galois[d.key_index[c]],
+                     d.keys[d.key_index[c]].seed if v == "regen" else None,
+                     kas[d.key_index[c]] if v == "stored" else None, outs[c]) for c in range(len(cts))]
+        # one multi-item call: ciphertexts of equal level share launches, and the launch
+        # sequences of different levels run concurrently on the library's four streams
+        res.update(both(lambda v: (lambda i, it=items_of(v): ctx.keyswitch_multi(it)), len(cts),
+                        "key_switches_per_s", None))
+
+        def single(v):
+            it = items_of(v)
+            return lambda i: [ctx.keyswitch(x[0][None], x[1], x[2], x[3], key_seed=x[4], key_a=x[5], out=x[6][None])
+                              for x in it]
+        one = both(single, len(cts), "key_switches_per_s", None)
+        for v in variants:
+            byts = sum(hbm_bytes(lv, 1, v == "regen") for lv in d.levels)
+            res[v]["hbm_roofline_frac"] = round(byts / (res[v]["ms_per_call"] * 1e-3) / HBM_PEAK, 4)
+            res[v]["one_call_per_ciphertext"] = {k: one[v][k] for k in ("key_switches_per_s", "ms_per_call",
+                                                                        "ms_median")}
+        res["key_set_bytes"] = {"regen": len(d.keys) * (DNUM * (L + K) * N * 4 + 32),
+                                "stored": 2 * len(d.keys) * DNUM * (L + K) * N * 4}
+    elif w == 6:
         # batch 8 at level 36: x (x) y, relinearisation with the s^2 key, rescale to level 35
         ctx = make_context(primes, BATCH, args)
         rng = np.random.default_rng(6006)
@@ -371,26 +506,12 @@ def other_workload(args) -> int:
         seed = rng.bytes(32)
         ka = ctx.expand_a(seed)
         out = torch.empty((BATCH, 2, LEVEL - 1, N), dtype=torch.int32, device="cuda")
-        for v in variants:
-            fn = lambda i, v=v: ctx.mul_relin_rescale(xs[0], xs[1], LEVEL, kb, key_seed=seed if v == "regen" else None,
-                                                       key_a=ka if v == "stored" else None, out=out)
-            ms = time_calls(fn, args.steps, args.warmup, torch)
-            ctx.profile(True)
-            for i in range(args.steps):
-                fn(i)
-            ctx.profile(False)
-            prof = ctx.profile_read()
-            res[v] = {"mul_relin_rescale_per_s": round(BATCH / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-        ms_r = time_calls(lambda i: ctx.rescale(xs[0], LEVEL, out=out), args.steps, args.warmup, torch)
-        ctx.profile(True)
-        for i in range(args.steps):
-            ctx.rescale(xs[0], LEVEL, out=out)
-        ctx.profile(False)
-        prof = ctx.profile_read()
-        res["rescale"] = {"ciphertexts_per_s": round(BATCH / (ms_r * 1e-3), 1), "ms_per_call": round(ms_r, 4),
-                          "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-    elif args.workload == 7:
+        res.update(both(lambda v: (lambda i: ctx.mul_relin_rescale(
+            xs[0], xs[1], LEVEL, kb, key_seed=seed if v == "regen" else None, key_a=ka if v == "stored" else None,
+            out=out)), BATCH, "mul_relin_rescale_per_s", ctx))
+        res["rescale"] = interleaved({"rescale": lambda i: ctx.rescale(xs[0], LEVEL, out=out)}, steps, warmup,
+                                     rounds, torch, ctx=ctx, items=BATCH, unit="ciphertexts_per_s")["rescale"]
+    elif w == 7:
         n1 = n2 = 4
         ctx = make_context(primes, BATCH, args)
         rng = np.random.default_rng(7007)
@@ -402,26 +523,21 @@ def other_workload(args) -> int:
         seeds = [rng.bytes(32) for _ in gs]
         kas = [ctx.expand_a(sd) for sd in seeds]
         out = torch.empty((2, LEVEL, N), dtype=torch.int32, device="cuda")
-        for v in variants:
+
+        def mk(v):
             keys = [(kbs[i], gs[i], seeds[i] if v == "regen" else None, kas[i] if v == "stored" else None)
                     for i in range(len(gs))]
-            fn = lambda i, keys=keys: ctx.linear_transform_bsgs(ct, LEVEL, diags, keys[:n1 - 1], keys[n1 - 1:], out=out)
-            ms = time_calls(fn, args.steps, args.warmup, torch)
-            ctx.profile(True)
-            for i in range(args.steps):
-                fn(i)
-            ctx.profile(False)
-            prof = ctx.profile_read()
-            res[v] = {"transforms_per_s": round(1 / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-                      "rotations_per_s": round((n1 * n2) / (ms * 1e-3), 1),
-                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-        t_diag = res[variants[0]]["kernel_ms"]["diag"] * 1e-3
+            return lambda i: ctx.linear_transform_bsgs(ct, LEVEL, diags, keys[:n1 - 1], keys[n1 - 1:], out=out)
+        res.update(both(mk, 1, "transforms_per_s", ctx))
+        for v in variants:
+            res[v]["rotations_per_s"] = round(n1 * n2 / (res[v]["ms_per_call"] * 1e-3), 1)
+        t_diag = res[variants[0]]["kernel_ms_per_call"]["diag"] * 1e-3
         # the diagonal sums read the diagonals and the baby steps and write the sums: n1*n2 + 2*(n1-1) + 2*n2
         # extended limbs; the giant-step sum (same timer class) reads n2 ciphertexts and writes one
         diag_bytes = ((n1 * n2 + 2 * (n1 - 1) + 2 * n2) * (LEVEL + K) + (n2 + 1) * 2 * LEVEL) * N * 4
         res["diag_roofline"] = {"bound": "hbm", "achieved_gbs": round(diag_bytes / t_diag / 1e9, 1),
                                 "peak_gbs": HBM_PEAK / 1e9, "frac": round(diag_bytes / t_diag / HBM_PEAK, 4)}
-    elif args.workload == 8:
+    elif w == 8:
         log_n8, l8, k8, d8 = SMALL_RING
         n8 = 1 << log_n8
         primes8 = chain_primes(log_n8, BITS, l8 + k8)
@@ -433,46 +549,102 @@ def other_workload(args) -> int:
         seed = rng.bytes(32)
         ka = ctx.expand_a(seed)
         out = torch.empty((BATCH, 2, l8, n8), dtype=torch.int32, device="cuda")
-        for v in variants:
-            fn = (lambda i, v=v: ctx.keyswitch(cts, l8, kb, GALOIS, key_seed=seed if v == "regen" else None,
-                                               key_a=ka if v == "stored" else None, out=out))
-            ms = time_calls(fn, args.steps, args.warmup, torch)
-            ctx.profile(True)
-            for i in range(args.steps):
-                fn(i)
-            ctx.profile(False)
-            prof = ctx.profile_read()
-            res[v] = {"key_switches_per_s": round(BATCH / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-                      "kernel_ms": {k: round(prof[k][0] / args.steps, 4) for k in prof if prof[k][1]}}
-    else:
-        ctx = make_context(primes, 16, args)
-        kbs = [to_device(synth.uniform_key_rows(5000 + k, primes, DNUM, N)) for k in range(len(d.keys))]
-        kas = [ctx.expand_a(kd.seed) for kd in d.keys] if "stored" in variants else None
-        cts = [to_device(c) for c in d.cts]
-        outs = [torch.empty((2, lv, N), dtype=torch.int32, device="cuda") for lv in d.levels]
-        for v in variants:
-            items = []
-            for c in range(len(cts)):
-                k = d.key_index[c]
-                items.append((cts[c], d.levels[c], kbs[k], wl.galois[k], d.keys[k].seed if v == "regen" else None,
-                              kas[k] if v == "stored" else None, outs[c]))
-            # one multi-item call: ciphertexts of equal level share launches, and the launch
-            # sequences of different levels run concurrently on the library's four streams
-            ms = time_calls(lambda i, items=items: ctx.keyswitch_multi(items), args.steps, args.warmup, torch)
-            # one call per ciphertext, for comparison
-            ms1 = time_calls(lambda i, items=items: [ctx.keyswitch(it[0][None], it[1], it[2], it[3], key_seed=it[4],
-                                                                   key_a=None if it[5] is None else it[5],
-                                                                   out=it[6][None]) for it in items],
-                             args.steps, args.warmup, torch)
-            byts = sum(hbm_bytes(lv, 1, v == "regen") for lv in d.levels)
-            res[v] = {"key_switches_per_s": round(len(cts) / (ms * 1e-3), 1), "ms_per_stream": round(ms, 4),
-                      "hbm_roofline_frac": round(byts / (ms * 1e-3) / HBM_PEAK, 4),
-                      "one_call_per_ciphertext": {"key_switches_per_s": round(len(cts) / (ms1 * 1e-3), 1),
-                                                  "ms_per_stream": round(ms1, 4)}}
-        res["key_set_bytes"] = {"regen": len(d.keys) * DNUM * (L + K) * N * 4,
-                                "stored": 2 * len(d.keys) * DNUM * (L + K) * N * 4}
-    print(json.dumps(res))
+        res.update(both(lambda v: (lambda i: ctx.keyswitch(cts, l8, kb, GALOIS, key_seed=seed if v == "regen" else None,
+                                                           key_a=ka if v == "stored" else None, out=out)),
+                        BATCH, "key_switches_per_s", ctx))
     ctx.close()
+    return res
+
+
+def valu_rates(torch) -> dict:
+    """Lane-op throughput (T/s) of each instruction kind of the microbenchmark library."""
+    import ctypes
+
+    torch.cuda.set_device(0)
+    torch.zeros(1, device="cuda")  # the HIP runtime torch loaded is the one the library binds to
+    lib = ctypes.CDLL(os.path.join(ROOT, "rns_ckks_key_amd", "libckks_valu_rates.so"))
+    lib.ckks_valu_rate_name.restype = ctypes.c_char_p
+    lib.ckks_valu_rate.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double)]
+    blocks, iters = 2048, 4096   # 8 waves on each of the 1,024 SIMDs; ~128 instructions x 4096 per thread
+    out = {"grid": {"workgroups": blocks, "threads_per_workgroup": 256, "iterations": iters,
+                    "instructions_per_iteration": 128, "independent_chains_per_lane": 8},
+           "peak_model_T_per_s": round(VALU_PEAK / 1e12, 3), "T_lane_ops_per_s": {}}
+    for op in range(lib.ckks_valu_rate_ops()):
+        v = ctypes.c_double()
+        rc = lib.ckks_valu_rate(op, blocks, iters, 5, ctypes.byref(v))
+        name = lib.ckks_valu_rate_name(op).decode()
+        out["T_lane_ops_per_s"][name] = round(v.value, 2) if rc == 0 else f"error {rc}"
+        print(f"[valu] {name}: {out['T_lane_ops_per_s'][name]}", file=sys.stderr, flush=True)
+    return out
+
+
+# ---------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--prewarm", type=float, default=2.0,
+                    help="seconds of alternating calls of both variants before any timing (clock settling)")
+    ap.add_argument("--rounds", type=int, default=4, help="alternating timed blocks of each variant after the headline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip workloads 3-5 in the default line")
+    ap.add_argument("--conv", choices=["vector", "matrix"], default="vector",
+                    help="base conversion on the vector unit or the matrix cores")
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4, 5, 6, 7, 8], default=2,
+                    help="2 (default, the headline): batch 8 at level 36; 3: level sweep; 4: hoisted 16 keys; "
+                         "5: mixed 64-ciphertext stream; 6: multiply + relinearise + rescale, batch 8 at level 36; "
+                         "7: 4 x 4 baby-step/giant-step linear transform at level 36; "
+                         "8: smaller ring N=2^15 (20+7 primes, dnum 3), batch 8 at level 20")
+    ap.add_argument("--variant", choices=["both", "regen", "stored"], default="both",
+                    help="which key variants to time (the headline is the regenerated one when it is timed)")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="only measure the lane-op throughput of the vector integer instructions the kernels use")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (xor with 0) three times, to calibrate HBM counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: key-switching is not sharded across GPUs in this library "
+              "(see the design notes); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        src = torch.randint(0, 2**31 - 1, (128 << 20,), dtype=torch.int32, device="cuda")  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_xor(src, 0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 3}))
+        return 0
+
+    if args.valu_rates:
+        print(json.dumps(valu_rates(torch)))
+        return 0
+
+    from rns_ckks_key_amd.api import chain_primes
+
+    torch.cuda.set_device(0)
+    primes = chain_primes(LOG_N, BITS, L + K)
+    if args.workload != 2:
+        print(json.dumps(run_workload(args.workload, args, primes, torch)))
+        return 0
+    out, host_inputs = headline(args, primes, torch)
+    if not args.no_extra:
+        out["workloads"] = {}
+        for w in (3, 4, 5):
+            r = run_workload(w, args, primes, torch)
+            print(f"[bench] workload {w} done", file=sys.stderr, flush=True)
+            out["workloads"][str(w)] = {k: v for k, v in r.items() if k not in ("n_gpus", "dtype", "data")}
+    if not args.no_cpu:
+        try:
+            out["cpu_baseline"] = cpu_baseline(primes, host_inputs["cts"], host_inputs["key_b"], host_inputs["seed"])
+        except Exception as e:  # the GPU line stands on its own; say why the baseline is missing
+            out["cpu_baseline"] = {"value": None, "unit": "key-switches/s", "kind": "oracle", "error": repr(e)}
+    print(json.dumps(out))
     return 0
 
 
