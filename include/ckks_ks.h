@@ -134,6 +134,24 @@ ckks_status ckks_keyswitch(const ckks_ctx *ctx, const uint32_t *ct, uint32_t lev
                            const uint8_t *key_seed, const uint32_t *key_a, uint32_t galois_elt,
                            uint32_t *out, uint32_t batch, void *stream);
 
+/* The key-switch of ckks_keyswitch for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): same arguments, same launches, bit-identical results, but
+ * its workspace is a static device array of the library (96 MiB per GPU,
+ * reserved on each GPU when the first context is created there and held until
+ * the process ends) instead of the context's; no call allocates or frees memory.
+ * The batch is limited by that array, not by max_batch: batch * (3*level +
+ * d_l*(L+K) + 2K) * N * 4 bytes must fit in it (one ciphertext at N = 2^16 with
+ * 36 + 12 primes at any level; more at lower levels and smaller rings).  Every
+ * call on one GPU uses the same array, so calls that overlap in time on one GPU
+ * (other streams, other threads, other contexts) race: serialise them.  No part
+ * of the array needs to start at zero; it keeps the last call's contents.
+ * Errors: as ckks_keyswitch, ERANGE when the batch does not fit the array, EHIP
+ * when the array has no address on the context's device. */
+ckks_status ckks_keyswitch_noalloc(const ckks_ctx *ctx, const uint32_t *ct, uint32_t level, const uint32_t *key_b,
+                                   const uint8_t *key_seed, const uint32_t *key_a, uint32_t galois_elt,
+                                   uint32_t *out, uint32_t batch, void *stream);
+
 /* Hoisted key-switch: one ModUp of ct[2][level][N], then for every key k an
  * inner product and ModDown with (key_b[k], key_a[k] or key_seeds[k], galois_elts[k]);
  * out is [n_keys][2][level][N], bit-identical to n_keys calls of ckks_keyswitch.

@@ -65,6 +65,7 @@ _SIGS = {
     "ckks_modup": (ctypes.c_int, [PCTX, P, U32, P, U32, P]),
     "ckks_moddown": (ctypes.c_int, [PCTX, P, U32, P, U32, P]),
     "ckks_keyswitch": (ctypes.c_int, [PCTX, P, U32, P, ctypes.c_char_p, P, U32, P, U32, P]),
+    "ckks_keyswitch_noalloc": (ctypes.c_int, [PCTX, P, U32, P, ctypes.c_char_p, P, U32, P, U32, P]),
     "ckks_keyswitch_hoisted": (ctypes.c_int, [PCTX, P, U32, U32, ctypes.POINTER(P), ctypes.c_char_p,
                                               ctypes.POINTER(P), PU32, P, P]),
     "ckks_expand_a": (ctypes.c_int, [PCTX, ctypes.c_char_p, P, P]),

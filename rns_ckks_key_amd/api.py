@@ -159,6 +159,19 @@ class Context:
                                  _ptr(out, (b, 2, level, self.n), "out"), b, _stream()))
         return out
 
+    def keyswitch_noalloc(self, ct: torch.Tensor, level: int, key_b: torch.Tensor, galois: int = 1,
+                          key_seed: bytes | None = None, key_a: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+        """keyswitch() with the library's static scratch array as workspace (the call allocates nothing)."""
+        b = ct.shape[0]
+        kshape = (self.dnum, self.L + self.K, self.n)
+        if out is None:
+            out = torch.empty((b, 2, level, self.n), dtype=torch.int32, device=ct.device)
+        check(lib.ckks_keyswitch_noalloc(self._h, _ptr(ct, (b, 2, level, self.n), "ct"), level,
+                                         _ptr(key_b, kshape, "key_b"), _seed(key_seed), _ptr(key_a, kshape, "key_a"),
+                                         galois, _ptr(out, (b, 2, level, self.n), "out"), b, _stream()))
+        return out
+
     def keyswitch_hoisted(self, ct: torch.Tensor, level: int, keys: list, out: torch.Tensor | None = None):
         """keys: list of (key_b, galois, key_seed or None, key_a or None)."""
         nk = len(keys)

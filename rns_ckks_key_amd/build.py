@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libckks_ks.so")
-SOURCES = ["kernels.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "noalloc.hip", "api.cpp"]
 # the integer-throughput microbenchmark behind the vector-ALU roofline (measurement only)
 RATES_LIB = os.path.join(HERE, "libckks_valu_rates.so")
 RATES_SRC = "valu_rates.hip"

@@ -806,6 +806,9 @@ ckks_status ckks_ctx_create(ckks_ctx** out, uint32_t log_n, uint32_t num_q, uint
     delete c;
     return fail(CKKS_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   }
+  // device address of the static scratch array of ckks_keyswitch_noalloc (once per
+  // device, with that device current); a failure only disables that call
+  (void)ckks::scratch_setup(c->device);
   ckks_status st = upload_tables(c);
   if (st != CKKS_OK) {
     std::string msg = g_err;
@@ -996,6 +999,35 @@ ckks_status ckks_keyswitch(const ckks_ctx* cc, const uint32_t* ct, uint32_t leve
       (st = check_batch(c, batch)) || (st = check_device(c)))
     return st;
   return keyswitch_run(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch, (hipStream_t)stream, nullptr);
+}
+
+ckks_status ckks_keyswitch_noalloc(const ckks_ctx* cc, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
+                                   const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt,
+                                   uint32_t* out, uint32_t batch, void* stream) {
+  ckks_ctx* c = const_cast<ckks_ctx*>(cc);
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_keyswitch_args(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch))) return st;
+  if (batch < 1) return fail(CKKS_ERANGE, "batch must be positive");
+  const Host& h = c->h;
+  const uint64_t N = h.n, d = digits_at(h, level), E = h.L + h.K;
+  // per ciphertext: rowtmp level limbs, ext d_l * (L+K), tmpP 2K, conv 2 * level
+  const uint64_t per_item = (level + d * E + 2ull * h.K + 2ull * level) * N;
+  const uint64_t need = per_item * batch * sizeof(uint32_t);
+  if (need > ckks::kScratchBytes)
+    return fail(CKKS_ERANGE, "batch %u at level %u needs %llu bytes of scratch, above the %llu-byte maximum", batch,
+                level, (unsigned long long)need, (unsigned long long)ckks::kScratchBytes);
+  if ((st = check_device(c))) return st;
+  uint32_t* sp = ckks::scratch_ptr(c->device);
+  if (!sp) return fail(CKKS_EHIP, "the static scratch array has no device address on device %d: %s", c->device,
+                       ckks::scratch_error(c->device));
+  Ws w{};
+  w.rowtmp = sp;
+  w.ext = w.rowtmp + (uint64_t)batch * level * N;
+  w.ext_item = d * E * N;
+  w.tmpP = w.ext + (uint64_t)batch * w.ext_item;
+  w.conv = w.tmpP + (uint64_t)batch * 2 * h.K * N;
+  return keyswitch_run(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch, (hipStream_t)stream, &w);
 }
 
 }  // extern "C"

@@ -174,5 +174,15 @@ hipError_t launch_sum(const DevTables& T, const SumArgs& a, uint32_t* out, uint3
 hipError_t launch_expand(const DevTables& T, const uint32_t seed[8], uint32_t* key_a, uint32_t regen_blocks,
                          hipStream_t s);
 
+// Static scratch of the key-switch that allocates nothing (noalloc.hip): 96 MiB per
+// GPU, the workspace of one ciphertext at N = 2^16 with 36 + 12 primes at any level.
+constexpr uint64_t kScratchBytes = 96ull << 20;
+// Looks up the array's device address on `device`, which must be current (once per
+// device; later calls return the first result).
+hipError_t scratch_setup(int device);
+// The array's device address on `device`, or nullptr if scratch_setup has not
+// succeeded there; scratch_error says why.
+uint32_t* scratch_ptr(int device);
+const char* scratch_error(int device);
 
 }  // namespace ckks

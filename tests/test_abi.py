@@ -201,3 +201,27 @@ def test_conv_mfma_switch_validates_the_shape():
     wide.close()
     assert lib.ckks_ctx_set_conv_mfma(None, 1) == EINVAL
 
+
+def test_noalloc_keyswitch_validates_before_any_launch():
+    # ckks_keyswitch_noalloc: the key-switch's checks, then its batch against the static
+    # scratch array (96 MiB per GPU), not against max_batch
+    boot = Context.for_chain(16, 36, 12, 3, 32, max_batch=0)
+    h = boot.handle
+    ct = ctypes.c_void_p(0x10000000)
+    out = ctypes.c_void_p(0x40000000)
+    kb = ctypes.c_void_p(0x70000000)
+    seed = bytes(32)
+
+    def nk(level=36, batch=1, ct=ct, out=out, g=5, sd=seed):
+        return lib.ckks_keyswitch_noalloc(h, ct, level, kb, sd, None, g, out, batch, None)
+
+    assert nk(batch=2) == ERANGE and "maximum" in lib.ckks_last_error().decode()  # 2 x 69 MiB
+    assert nk(level=4, batch=4) == EINVAL and "host-only" in lib.ckks_last_error().decode()  # 4 x 21 MiB fits
+    assert nk(level=4, batch=5) == ERANGE
+    assert nk(batch=0) == ERANGE
+    assert nk(level=37) == ERANGE
+    assert nk(g=10) == ERANGE
+    assert nk(sd=None) == EINVAL
+    assert nk(out=ct) == EINVAL and "overlaps ct" in lib.ckks_last_error().decode()
+    assert nk() == EINVAL and "host-only" in lib.ckks_last_error().decode()
+    boot.close()
