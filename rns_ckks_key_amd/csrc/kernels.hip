@@ -179,21 +179,24 @@ __device__ __forceinline__ void lds_get_B(uint32_t (&x)[16], const uint32_t* lds
 
 // ------------------------------------------------------------------ row pass
 
-// Forward stages 512..1 of block `blk` of one limb: layout A in, layout C out.
-// Twiddle of a butterfly whose first element is at e = blk*1024 + r with half
-// distance t: tw[N/(2t) + e/(2t)].  The butterflies carry lazy values; CANON makes
-// the outputs canonical (callers that only multiply them by constants skip it).
-template <bool CANON = true>
-__device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32_t blk, const uint32_t* __restrict__ tw,
-                                        uint32_t q, uint32_t qinv, uint32_t n, uint32_t* lds, uint2 one) {
+// Forward stages 512..1 of one 1024-block of a limb: layout A in, layout C out.
+// A stage of half distance t has m = 512/t twiddle groups in a block; group i of
+// block blk uses tw[N/(2t) + blk*m + i] = tw[m*(N/1024 + blk) + i].  The caller
+// passes `off`: N/1024 + blk with the limb's table, or 1 with a block's own copy
+// (entry m + i, as staged in LDS by stage_block_twiddles).  The butterflies carry
+// lazy values; CANON makes the outputs canonical (callers that only multiply them
+// by constants skip it).  BIG: the prime exceeds 2^31, known at compile time, so
+// canonical is one conditional subtraction with no branch on q.
+template <bool CANON = true, bool BIG = false>
+__device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32_t off, const uint32_t* __restrict__ tw,
+                                        uint32_t q, uint32_t qinv, uint32_t* lds, uint2 one) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int h = 8 >> s;
-    const uint32_t t = 512u >> s;
-    const uint32_t base = n / (2 * t) + blk * (512u / t);
+    const uint32_t m = 1u << s;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = tw[base + grp];
+      const uint32_t w = tw[m * off + grp];
 #pragma unroll
       for (int kk = 0; kk < h; ++kk) ct_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
     }
@@ -206,8 +209,8 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int h = 8 >> s;
-    const uint32_t t = 32u >> s;
-    const uint32_t base = n / (2 * t) + blk * (512u / t) + 8 * hb / h;
+    const uint32_t m = 16u << s;
+    const uint32_t base = m * off + 8 * hb / h;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
       const uint32_t w = tw[base + grp];
@@ -221,30 +224,33 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
   wave_sync();
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const uint32_t w = tw[n / 4 + blk * 256 + lane + 64 * g];
+    const uint32_t w = tw[256 * off + lane + 64 * g];
     ct_bfly(x[4 * g], x[4 * g + 2], w, qinv, q);
     ct_bfly(x[4 * g + 1], x[4 * g + 3], w, qinv, q);
-    const uint32_t i1 = n / 2 + blk * 512 + 2 * lane + 128 * g;
+    const uint32_t i1 = 512 * off + 2 * lane + 128 * g;
     const uint32_t w0 = tw[i1], w1 = tw[i1 + 1];
     ct_bfly(x[4 * g], x[4 * g + 1], w0, qinv, q);
     ct_bfly(x[4 * g + 2], x[4 * g + 3], w1, qinv, q);
   }
-  if constexpr (CANON) {
+  if constexpr (CANON && BIG) {
+    canon_big(x, q);
+  } else if constexpr (CANON) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) x[k] = canon(x[k], q, one.x, one.y);
   }
 }
 
-// Inverse stages 1..512 of block `blk`: layout C in, layout A out (no N^-1).
-__device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32_t blk, const uint32_t* __restrict__ itw,
-                                        uint32_t q, uint32_t qinv, uint32_t n, uint32_t* lds) {
+// Inverse stages 1..512 of one 1024-block: layout C in, layout A out (no N^-1).
+// Twiddles indexed as in row_fwd (off = N/1024 + blk, or 1 with a block's copy).
+__device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32_t off, const uint32_t* __restrict__ itw,
+                                        uint32_t q, uint32_t qinv, uint32_t* lds) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const uint32_t i1 = n / 2 + blk * 512 + 2 * lane + 128 * g;
+    const uint32_t i1 = 512 * off + 2 * lane + 128 * g;
     const uint32_t w0 = itw[i1], w1 = itw[i1 + 1];
     gs_bfly(x[4 * g], x[4 * g + 1], w0, qinv, q);
     gs_bfly(x[4 * g + 2], x[4 * g + 3], w1, qinv, q);
-    const uint32_t w = itw[n / 4 + blk * 256 + lane + 64 * g];
+    const uint32_t w = itw[256 * off + lane + 64 * g];
     gs_bfly(x[4 * g], x[4 * g + 2], w, qinv, q);
     gs_bfly(x[4 * g + 1], x[4 * g + 3], w, qinv, q);
   }
@@ -256,8 +262,8 @@ __device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int h = 1 << s;
-    const uint32_t t = 4u << s;
-    const uint32_t base = n / (2 * t) + blk * (512u / t) + 8 * hb / h;
+    const uint32_t m = 128u >> s;
+    const uint32_t base = m * off + 8 * hb / h;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
       const uint32_t w = itw[base + grp];
@@ -272,14 +278,23 @@ __device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int h = 1 << s;
-    const uint32_t t = 64u << s;
-    const uint32_t base = n / (2 * t) + blk * (512u / t);
+    const uint32_t m = 8u >> s;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = itw[base + grp];
+      const uint32_t w = itw[m * off + grp];
 #pragma unroll
       for (int kk = 0; kk < h; ++kk) gs_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
     }
+  }
+}
+
+// Copies the twiddles of block blk of a limb (entries m*(N/1024 + blk) + i of its
+// table, m = 1, 2, ..., 512, i < m) to dst[m + i]: the 1023 twiddles a row pass over
+// that block uses.  Every thread of the workgroup may take part (no barrier here).
+__device__ __forceinline__ void stage_block_twiddles(uint32_t* dst, const uint32_t* __restrict__ tw, uint32_t off) {
+  for (uint32_t k = threadIdx.x + 1; k < kRow; k += blockDim.x) {
+    const uint32_t m = 1u << (31 - __builtin_clz(k));  // the stage of entry k: m <= k < 2m
+    dst[k] = tw[m * off + (k - m)];
   }
 }
 
@@ -404,8 +419,9 @@ __device__ __forceinline__ void place_block(const uint32_t (&w)[16], uint32_t po
 // all threads (block j of tile T by job T*nb + j); a workgroup prefix sum of the
 // accepted counts places each block's words.  The rare tile still short of 1024
 // words continues with blockDim.x more blocks at a time.  cnt: LDS scratch of
-// 2*ntiles + 16 + blockDim.x words.  Every thread of the workgroup must call
-// this (it contains workgroup barriers).
+// 2*ntiles + 16 + 64 words (the last 64: one sink word per lane, shared by the
+// waves, as only lanes of one instruction write at once).  Every thread of the
+// workgroup must call this (it contains workgroup barriers).
 __device__ void regen_tiles(const uint32_t* __restrict__ seed, uint32_t j0, uint32_t ntiles, uint32_t t,
                             uint32_t tau, uint32_t q, uint32_t bound, uint2 one, uint32_t nb, uint32_t* dst,
                             uint32_t* cnt) {
@@ -414,7 +430,7 @@ __device__ void regen_tiles(const uint32_t* __restrict__ seed, uint32_t j0, uint
   uint32_t* tstart = cnt;             // [ntiles] accepted words before each tile's first block
   uint32_t* tot = cnt + ntiles;       // [ntiles] accepted words of the first nb blocks of each tile
   uint32_t* wsum = cnt + 2 * ntiles;  // [16] scan scratch
-  uint32_t* trash = cnt + 2 * ntiles + 16 + tid;  // this thread's sink for words that land nowhere
+  uint32_t* trash = cnt + 2 * ntiles + 16 + (tid & 63);  // this lane's sink for words that land nowhere
   uint32_t carry = 0;                 // accepted words of all earlier passes (uniform)
   for (uint32_t r0 = 0; r0 < jobs; r0 += nth) {
     const uint32_t x = r0 + tid;
@@ -463,7 +479,8 @@ __device__ void regen_tiles(const uint32_t* __restrict__ seed, uint32_t j0, uint
 
 // MUL (inverse only): the source limb is the product of src and src2 (same layout), the
 // x1*y1 part of a tensor product formed where the relinearisation's ModUp reads it.
-template <bool FWD, bool MUL = false>
+// BIG (forward only): every prime of the chain exceeds 2^31.
+template <bool FWD, bool MUL = false, bool BIG = false>
 __global__ __launch_bounds__(256) void k_row(DevTables T, RowArgs a) {
   __shared__ uint32_t lds[4][kRowPad];
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -489,7 +506,7 @@ __global__ __launch_bounds__(256) void k_row(DevTables T, RowArgs a) {
   uint32_t x[16];
   if (FWD) {
     load_A(x, src, lane);
-    row_fwd(x, lane, blk, T.tw + (uint64_t)tp * n, q, T.qinv[tp], n, lds[wave], T.one[tp]);
+    row_fwd<true, BIG>(x, lane, n / kRow + blk, T.tw + (uint64_t)tp * n, q, T.qinv[tp], lds[wave], T.one[tp]);
     if (a.cmb) {
       const uint2 f = a.cmb_factor[y];
       uint32_t c[16];
@@ -513,7 +530,7 @@ __global__ __launch_bounds__(256) void k_row(DevTables T, RowArgs a) {
         x[4 * g + 3] = prod_mod(x[4 * g + 3], v.w, md, r2);
       }
     }
-    row_inv(x, lane, blk, T.itw + (uint64_t)tp * n, q, T.qinv[tp], n, lds[wave]);
+    row_inv(x, lane, n / kRow + blk, T.itw + (uint64_t)tp * n, q, T.qinv[tp], lds[wave]);
     store_A(dst, x, lane);
   }
 }
@@ -889,7 +906,9 @@ __device__ __forceinline__ uint32_t galois_src(uint32_t j, uint32_t g, uint32_t 
 // TENSOR (final pass of a relinearisation): the ciphertext is the tensor product
 // (x0 y0, x0 y1 + x1 y0, x1 y1) of ct = x and a.ty = y, formed here from x and y:
 // x0 y0 is the c0 term, x1 y1 the own digit, and x0 y1 + x1 y0 is added to the a-half.
-template <bool FINAL, int WAVES, bool TENSOR = false>
+// BIG: every prime of the chain exceeds 2^31 (the canonical form of conv's transform
+// then needs no branch on q).
+template <bool FINAL, int WAVES, bool TENSOR = false, bool BIG = false>
 __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
   extern __shared__ uint32_t smem[];
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -914,8 +933,17 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
   const uint32_t tile_words = (a_in_lds ? nd * kRow : 0u) + (kStage ? nd * kRow : 0u);
   uint32_t* Atile = smem;                                   // a rows [nd][1024]
   uint32_t* Btile = smem + nd * kRow;                       // b rows [nd][1024] (staged only)
-  uint32_t* priv = smem + tile_words + wave * kRowPad;      // wave-private block
-  uint32_t* cnt = smem + tile_words + WAVES * kRowPad;      // expander scratch
+  // Several waves also share the twiddles of this prime's blocks: the final pass's
+  // conv transform uses block blk, the digits' transforms block sblk (their source
+  // under sigma_g), the special pass's inverse transform block blk.  Staged in LDS
+  // (two tables of 1024 words), they replace per-lane loads from the limb's table
+  // in the middle of each transform.
+  uint32_t* twA = smem + tile_words;                        // sblk's forward twiddles (staged only)
+  uint32_t* twB = twA + kRow;                               // blk's forward (FINAL) or inverse twiddles
+  const uint32_t stw = kStage ? 2 * kRow : 0u;
+  uint32_t* priv = smem + tile_words + stw + wave * kRowPad;  // wave-private block
+  uint32_t* cnt = smem + tile_words + stw + WAVES * kRowPad;  // expander scratch
+  const uint32_t sblk = galois_src(blk * kRow, key.galois, T.log_n) >> 10;
 
   if (kStage) {
     for (uint32_t i = threadIdx.x; i < nd * (kRow / 4); i += blockDim.x) {
@@ -924,6 +952,8 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
       *reinterpret_cast<uint4*>(Btile + j * kRow + 4 * w4) = *reinterpret_cast<const uint4*>(key.b + off);
       if (key.a) *reinterpret_cast<uint4*>(Atile + j * kRow + 4 * w4) = *reinterpret_cast<const uint4*>(key.a + off);
     }
+    stage_block_twiddles(twA, tw, n / kRow + sblk);
+    stage_block_twiddles(twB, FINAL ? tw : T.itw + (uint64_t)tabs * n, n / kRow + blk);
   }
   if (!key.a) {
     uint32_t seed[8];
@@ -931,13 +961,17 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
     regen_tiles(seed, 0, nd, tabs, blk, q, T.bound[tabs], T.one[tabs], a.regen_blocks, Atile, cnt);
   }
   __syncthreads();
+  // twiddle sources and offsets of the three kinds of row transform
+  const uint32_t* tw_dig = kStage ? twA : tw;
+  const uint32_t off_dig = kStage ? 1u : n / kRow + sblk;
+  const uint32_t* tw_blk = kStage ? twB : (FINAL ? tw : T.itw + (uint64_t)tabs * n);
+  const uint32_t off_blk = kStage ? 1u : n / kRow + blk;
   const uint32_t* kb_row = kStage ? Btile : key.b + (uint64_t)tabs * n + blk * kRow;
   const uint32_t* ka_row = a_in_lds ? Atile : key.a + (uint64_t)tabs * n + blk * kRow;
   const uint64_t bstride = kStage ? kRow : (uint64_t)E * n;   // digit stride of kb_row
   const uint64_t kstride = a_in_lds ? kRow : (uint64_t)E * n; // digit stride of ka_row
 
   // this lane's 16 output positions (layout C) and their sources under sigma_g
-  const uint32_t sblk = galois_src(blk * kRow, key.galois, T.log_n) >> 10;
   uint32_t sidx[16];  // padded LDS position of each output's source within block sblk
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -964,9 +998,9 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
     uint32_t rb[16], ra[16];
     if constexpr (FINAL) {
       load_A(rb, a.conv + (((uint64_t)item * 2 + 0) * level + limb) * n + blk * kRow, lane);
-      row_fwd<(WAVES > 1)>(rb, lane + opaque_zero(), blk, tw, q, md.qinv, n, priv, T.one[tabs]);
+      row_fwd<(WAVES > 1), BIG>(rb, lane + opaque_zero(), off_blk, tw_blk, q, md.qinv, priv, T.one[tabs]);
       load_A(ra, a.conv + (((uint64_t)item * 2 + 1) * level + limb) * n + blk * kRow, lane);
-      row_fwd<(WAVES > 1)>(ra, lane + opaque_zero(), blk, tw, q, md.qinv, n, priv, T.one[tabs]);
+      row_fwd<(WAVES > 1), BIG>(ra, lane + opaque_zero(), off_blk, tw_blk, q, md.qinv, priv, T.one[tabs]);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) { rb[r] = 0; ra[r] = 0; }
@@ -992,7 +1026,7 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
         }
       } else {
         load_A(x, ext + ((uint64_t)j * E + elimb) * n + sblk * kRow, lane);
-        row_fwd<false>(x, lane + opaque_zero(), sblk, tw, q, md.qinv, n, priv, T.one[tabs]);  // lazy: only multiplied
+        row_fwd<false>(x, lane + opaque_zero(), off_dig, tw_dig, q, md.qinv, priv, T.one[tabs]);  // lazy: only multiplied
       }
       lds_put_C(priv, x, lane);
       wave_sync();
@@ -1023,11 +1057,10 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
       wave_sync();
     }
     if (!FINAL) {
-      const uint32_t* itw = T.itw + (uint64_t)tabs * n;
-      row_inv(rb, lane + opaque_zero(), blk, itw, q, md.qinv, n, priv);
+      row_inv(rb, lane + opaque_zero(), off_blk, tw_blk, q, md.qinv, priv);
       store_A(a.tmpP + (((uint64_t)item * 2 + 0) * K + limb) * n + blk * kRow, rb, lane);
       __builtin_amdgcn_sched_barrier(0);
-      row_inv(ra, lane + opaque_zero(), blk, itw, q, md.qinv, n, priv);
+      row_inv(ra, lane + opaque_zero(), off_blk, tw_blk, q, md.qinv, priv);
       store_A(a.tmpP + (((uint64_t)item * 2 + 1) * K + limb) * n + blk * kRow, ra, lane);
     } else {
       // -(2^32 P^-1) in Montgomery form: the accumulators hold conv - sum
@@ -1083,14 +1116,14 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
 // A batch sharing one key, whose tiles are staged once in LDS per workgroup.
 // Eight waves, at most 128 VGPRs: the tiles' LDS is shared by eight waves, so two
 // workgroups (four waves per SIMD) fit a CU.
-template <bool FINAL, bool TENSOR = false>
+template <bool FINAL, bool TENSOR = false, bool BIG = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_ip8(DevTables T, IpArgs a) {
-  ip_body<FINAL, 8, TENSOR>(T, a);
+  ip_body<FINAL, 8, TENSOR, BIG>(T, a);
 }
 // Four waves (batches of 4..7): LDS allows three workgroups per CU.
-template <bool FINAL, bool TENSOR = false>
+template <bool FINAL, bool TENSOR = false, bool BIG = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_ip4(DevTables T, IpArgs a) {
-  ip_body<FINAL, 4, TENSOR>(T, a);
+  ip_body<FINAL, 4, TENSOR, BIG>(T, a);
 }
 // One wave per workgroup (hoisted keys, multi-item groups, small batches).  At
 // least two waves per SIMD: the register budget that keeps the single-wave shapes
@@ -1265,7 +1298,7 @@ __global__ __launch_bounds__(256) void k_sum(DevTables T, SumArgs a, uint32_t* _
 // Standalone expansion of the a-half: grid x = tile, y = prime, z = digit.
 __global__ __launch_bounds__(64) void k_expand(DevTables T, KeyRef key, uint32_t* key_a, uint32_t nb) {
   __shared__ uint32_t tile[kRow];
-  __shared__ uint32_t cnt[2 + 16 + 64];  // regen_tiles scratch for one tile and 64 threads
+  __shared__ uint32_t cnt[2 + 16 + 64];  // regen_tiles scratch for one tile
   const uint32_t tau = blockIdx.x, t = blockIdx.y, j = blockIdx.z;
   uint32_t seed[8];
   for (int i = 0; i < 8; ++i) seed[i] = key.seed[i];
@@ -1305,7 +1338,8 @@ hipError_t launch_row(const DevTables& T, const RowArgs& a, bool fwd, uint32_t i
   const uint32_t nblk = T.n / kRow;
   dim3 grid((nblk + 3) / 4, a.n_limbs, items);
   if (a.src2 && (fwd || a.use_srcs || a.own_n)) return hipErrorInvalidValue;  // products: plain inverse only
-  if (fwd) hipLaunchKernelGGL(k_row<true>, grid, dim3(256), 0, s, T, a);
+  if (fwd && T.all_big) hipLaunchKernelGGL((k_row<true, false, true>), grid, dim3(256), 0, s, T, a);
+  else if (fwd) hipLaunchKernelGGL(k_row<true>, grid, dim3(256), 0, s, T, a);
   else if (a.src2) hipLaunchKernelGGL((k_row<false, true>), grid, dim3(256), 0, s, T, a);
   else hipLaunchKernelGGL(k_row<false>, grid, dim3(256), 0, s, T, a);
   return hipGetLastError();
@@ -1413,14 +1447,20 @@ hipError_t launch_ip(const DevTables& T, const IpArgs& a, bool final_pass, uint3
   const uint32_t nth = 64 * waves;
   bool regen = false;
   for (uint32_t k = 0; k < a.n_keys; ++k) regen |= a.key[k].a == nullptr;
-  const size_t tiles = (waves > 1 ? 2 * (size_t)a.nd * kRow : (regen ? (size_t)a.nd * kRow : 0));
-  const size_t shm = (tiles + waves * kRowPad + (regen ? 2 * a.nd + 16 + nth : 0)) * sizeof(uint32_t);
+  // staged key rows and two block twiddle tables (multi-wave), or a regenerated a-half
+  const size_t tiles = (waves > 1 ? 2 * ((size_t)a.nd + 1) * kRow : (regen ? (size_t)a.nd * kRow : 0));
+  const size_t shm = (tiles + waves * kRowPad + (regen ? 2 * a.nd + 16 + 64 : 0)) * sizeof(uint32_t);
+  const bool big = T.all_big;  // the multi-wave final passes canonicalise conv's transform without a branch on q
   if (final_pass) {
     if (a.ty) {  // relinearisation of the tensor product of ct and ty
-      if (waves == 8) hipLaunchKernelGGL((k_ip8<true, true>), grid, dim3(nth), shm, s, T, a);
+      if (waves == 8 && big) hipLaunchKernelGGL((k_ip8<true, true, true>), grid, dim3(nth), shm, s, T, a);
+      else if (waves == 8) hipLaunchKernelGGL((k_ip8<true, true>), grid, dim3(nth), shm, s, T, a);
+      else if (waves == 4 && big) hipLaunchKernelGGL((k_ip4<true, true, true>), grid, dim3(nth), shm, s, T, a);
       else if (waves == 4) hipLaunchKernelGGL((k_ip4<true, true>), grid, dim3(nth), shm, s, T, a);
       else hipLaunchKernelGGL((k_ip1<true, true>), grid, dim3(nth), shm, s, T, a);
-    } else if (waves == 8) hipLaunchKernelGGL((k_ip8<true>), grid, dim3(nth), shm, s, T, a);
+    } else if (waves == 8 && big) hipLaunchKernelGGL((k_ip8<true, false, true>), grid, dim3(nth), shm, s, T, a);
+    else if (waves == 8) hipLaunchKernelGGL((k_ip8<true>), grid, dim3(nth), shm, s, T, a);
+    else if (waves == 4 && big) hipLaunchKernelGGL((k_ip4<true, false, true>), grid, dim3(nth), shm, s, T, a);
     else if (waves == 4) hipLaunchKernelGGL((k_ip4<true>), grid, dim3(nth), shm, s, T, a);
     else hipLaunchKernelGGL((k_ip1<true>), grid, dim3(nth), shm, s, T, a);
   } else {
