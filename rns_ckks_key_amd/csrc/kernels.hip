@@ -633,23 +633,41 @@ __device__ __forceinline__ void col_fwd_lanes(uint32_t (&v)[(1 << LOGC) / G], co
 // values on the column's C rows (sum over sources of y_s * c_s, reduced), then its
 // column NTT, stored.  G consecutive lanes (G = 1, 2 or 4) share the task: lane z
 // holds rows z + G*i.
-template <int LOGC, int CW, int MAXS, int G, bool BIG>
-__device__ __forceinline__ void conv_task(const DevTables& T, const ConvArgs& a, const uint32_t* ys, uint32_t* dst,
-                                          uint32_t e, uint32_t c, uint32_t z, uint32_t ns, uint32_t skip_lo,
-                                          uint32_t col0, uint32_t y) {
-  constexpr int C = 1 << LOGC, R = C / G;
-  const uint32_t n = T.n;
-  const uint32_t dl = (a.skip && e >= skip_lo) ? e + ns : e;
-  const uint32_t tp = a.level ? (dl < a.level ? dl : T.L + (dl - a.level)) : dl;
-  const Mod md{T.q[tp], T.qinv[tp]};
-  const uint32_t* cv = a.conv + y * a.conv_y + (a.conv_by_abs ? tp : dl);
+// The target of a task: its destination limb, prime, and the conversion constants
+// of every source split into 16-bit halves (zero past the last source).
+template <int MAXS>
+struct ConvTarget {
   uint32_t cl[MAXS], ch[MAXS];
+  Mod md;
+  uint32_t dl, tp;
+};
+
+template <int MAXS>
+__device__ __forceinline__ ConvTarget<MAXS> conv_target(const DevTables& T, const ConvArgs& a, uint32_t e, uint32_t ns,
+                                                        uint32_t skip_lo, uint32_t y) {
+  ConvTarget<MAXS> k;
+  k.dl = (a.skip && e >= skip_lo) ? e + ns : e;
+  k.tp = a.level ? (k.dl < a.level ? k.dl : T.L + (k.dl - a.level)) : k.dl;
+  k.md = Mod{T.q[k.tp], T.qinv[k.tp]};
+  const uint32_t* cv = a.conv + y * a.conv_y + (a.conv_by_abs ? k.tp : k.dl);
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     const uint32_t w = (uint32_t)s < ns ? cv[s * a.conv_s] : 0u;  // zero weight past the last source
-    cl[s] = w & 0xffffu;
-    ch[s] = w >> 16;
+    k.cl[s] = w & 0xffffu;
+    k.ch[s] = w >> 16;
   }
+  return k;
+}
+
+template <int LOGC, int CW, int MAXS, int G, bool BIG>
+__device__ __forceinline__ void conv_task(const DevTables& T, const ConvArgs& a, const uint32_t* ys, uint32_t* dst,
+                                          const ConvTarget<MAXS>& k, uint32_t c, uint32_t z, uint32_t col0) {
+  constexpr int C = 1 << LOGC, R = C / G;
+  const uint32_t n = T.n;
+  const uint32_t dl = k.dl, tp = k.tp;
+  const Mod md = k.md;
+  const uint32_t* cl = k.cl;
+  const uint32_t* ch = k.ch;
   uint32_t v[R];
   static_for<R>([&](auto kc) {
     constexpr int i = decltype(kc)::value;
@@ -698,21 +716,6 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const uint32_t p0 = a.src_prime0 + y * a.src_prime_step;
   const uint32_t ns = min(a.ns_max, a.ns_limit - y * a.src_prime_step);
   const uint32_t* src = a.src + item * a.src_item + y * a.src_y;
-  for (uint32_t task = threadIdx.x; task < ns * CW; task += blockDim.x) {
-    const uint32_t s = task / CW, c = task - s * CW;
-    const uint32_t tp = p0 + s;
-    const uint32_t q = T.q[tp];
-    uint32_t v[C];
-    const uint32_t* ps = src + (uint64_t)s * n + col0 + c;
-#pragma unroll
-    for (int k = 0; k < C; ++k) v[k] = ps[k * kRow];
-    col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
-    const uint2 sc = a.scale[y * a.scale_y + s];
-#pragma unroll
-    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = mul_const(v[k], sc.x, sc.y, q);
-  }
-  __syncthreads();
-  uint32_t* dst = a.dst + item * a.dst_item + y * a.dst_y;
   // ModUp: the digit's own limbs [p0, p0 + ns) of the extended basis are not targets
   const uint32_t skip_lo = p0;
   const uint32_t n_targets = a.skip ? a.level + T.K - ns : a.n_targets;
@@ -724,14 +727,43 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const uint32_t full = ntask / nth * nth, rem = ntask - full;
   const uint32_t G = (LOGC >= 4 && rem) ? (nth >= 4 * rem ? 4u : nth >= 2 * rem ? 2u : 1u) : 1u;
   const bool coop = G > 1;
-  for (uint32_t task = threadIdx.x; task < (coop ? full : ntask); task += nth)
-    conv_task<LOGC, CW, MAXS, 1, BIG>(T, a, ys, dst, e0 + task / CW, task % CW, 0, ns, skip_lo, col0, y);
+  const uint32_t nfirst = coop ? full : ntask;
+  // Phase 1: one (source, column) task per thread (ns * CW <= 256 <= NTH).  The
+  // threads without one load the constants of their first phase-2 task meanwhile,
+  // so that latency passes during phase 1 (on the phase-1 path they are not live).
+  static_assert(16 * CW <= NTH, "one phase-1 task per thread");
+  const bool has_first = threadIdx.x < nfirst;
+  ConvTarget<MAXS> first;
+  const uint32_t task1 = threadIdx.x;
+  if (task1 >= ns * CW) {
+    if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
+  } else {
+    const uint32_t task = task1;
+    const uint32_t s = task / CW, c = task - s * CW;
+    const uint32_t tp = p0 + s;
+    const uint32_t q = T.q[tp];
+    uint32_t v[C];
+    const uint32_t* ps = src + (uint64_t)s * n + col0 + c;
+#pragma unroll
+    for (int k = 0; k < C; ++k) v[k] = ps[k * kRow];
+    col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
+    const uint2 sc = a.scale[y * a.scale_y + s];
+#pragma unroll
+    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = mul_const(v[k], sc.x, sc.y, q);
+    if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
+  }
+  __syncthreads();
+  uint32_t* dst = a.dst + item * a.dst_item + y * a.dst_y;
+  if (has_first) conv_task<LOGC, CW, MAXS, 1, BIG>(T, a, ys, dst, first, threadIdx.x % CW, 0, col0);
+  for (uint32_t task = threadIdx.x + nth; task < nfirst; task += nth)
+    conv_task<LOGC, CW, MAXS, 1, BIG>(T, a, ys, dst, conv_target<MAXS>(T, a, e0 + task / CW, ns, skip_lo, y),
+                                      task % CW, 0, col0);
   if constexpr (LOGC >= 4) {
     if (coop && threadIdx.x < rem * G) {  // whole groups of G lanes: G divides 64
       const uint32_t task = full + threadIdx.x / G, z = threadIdx.x % G;
-      const uint32_t e = e0 + task / CW, c = task % CW;
-      if (G == 2) conv_task<LOGC, CW, MAXS, 2, BIG>(T, a, ys, dst, e, c, z, ns, skip_lo, col0, y);
-      else conv_task<LOGC, CW, MAXS, 4, BIG>(T, a, ys, dst, e, c, z, ns, skip_lo, col0, y);
+      const ConvTarget<MAXS> k = conv_target<MAXS>(T, a, e0 + task / CW, ns, skip_lo, y);
+      if (G == 2) conv_task<LOGC, CW, MAXS, 2, BIG>(T, a, ys, dst, k, task % CW, z, col0);
+      else conv_task<LOGC, CW, MAXS, 4, BIG>(T, a, ys, dst, k, task % CW, z, col0);
     }
   }
 }
