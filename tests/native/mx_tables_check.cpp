@@ -1,6 +1,6 @@
 // Host check of the matrix-core conversion's operand tables (no GPU).
 //
-// The library's host code is compiled in (api.cpp, launchers stubbed out).  For the
+// The library's host code is compiled in (api.cpp, launchers and the no-alloc scratch stubbed out).  For the
 // N = 2^16, 36 + 12 prime chain it builds the tables, then emulates what the
 // conversion kernel computes from them: the int8 product of a constant tile (A) and
 // the 7-bit digits of 32 coefficients' source values (B), in the lane layout of
@@ -34,6 +34,10 @@ hipError_t launch_sum(const DevTables&, const SumArgs&, uint32_t*, uint32_t, hip
 hipError_t launch_expand(const DevTables&, const uint32_t*, uint32_t*, uint32_t, hipStream_t) {
   return hipErrorInvalidValue;
 }
+// the no-alloc key-switch's static array lives in device code, not compiled here
+hipError_t scratch_setup(int) { return hipErrorInvalidValue; }
+uint32_t* scratch_ptr(int) { return nullptr; }
+const char* scratch_error(int) { return "not built into the host check"; }
 }  // namespace ckks
 
 namespace {
