@@ -453,6 +453,28 @@ def run_workload(w: int, args, primes, torch) -> dict:
                 r[v]["hbm_roofline_frac"] = round(hbm_bytes(level, 16, v == "regen") / (r[v]["ms_per_call"] * 1e-3)
                                                   / HBM_PEAK, 4)
             res["levels"][str(level)] = r
+        # the same calls with the inner product and ModDown as separate launches, once, for the
+        # per-step split the fused kernels hide: NTT = every row pass (the column halves are fused
+        # into the conversions), ModUp = its conversion, inner product alone, ModDown = its
+        # conversion and its final row NTT with the subtraction and P^-1
+        ctx.set_fused(False)
+        res["unfused_split"] = {}
+        steps_of = {"ntt": ("row", "digit_ntt", "moddown_row"), "modup": ("modup_conv",),
+                    "inner_product": ("ip_ext",), "moddown": ("moddown_conv", "moddown_final")}
+        for li, level in enumerate(wl.levels):
+            cts = to_device(np.stack(d.cts[16 * li:16 * li + 16]))
+            out = torch.empty((16, 2, level, N), dtype=torch.int32, device="cuda")
+            mk = (lambda v, lv=level, c=cts, o=out: lambda i: ctx.keyswitch(
+                c, lv, kb, 5, key_seed=seed if v == "regen" else None, key_a=ka if v == "stored" else None, out=o))
+            r = both(mk, 16, "key_switches_per_s", ctx)
+            for v in r:
+                k = r[v]["kernel_ms_per_call"]
+                r[v] = {"ms_per_call": r[v]["ms_per_call"], "ms_median": r[v]["ms_median"],
+                        "step_ms_per_call": {st: round(sum(k.get(c, 0.0) for c in cs), 4)
+                                             for st, cs in steps_of.items()},
+                        "kernel_ms_per_call": k}
+            res["unfused_split"][str(level)] = r
+        ctx.set_fused(True)
     elif w == 4:
         ctx = make_context(primes, 16, args)
         ct = to_device(d.cts[0])

@@ -269,6 +269,22 @@ ckks_status ckks_ctx_set_regen_blocks(ckks_ctx *ctx, uint32_t blocks);
  * Errors: EINVAL (NULL ctx, host-only context), EUNSUPPORTED (on = 1 for another shape). */
 ckks_status ckks_ctx_set_conv_mfma(ckks_ctx *ctx, uint32_t on);
 
+/* Fusion of the inner product with ModDown in ckks_keyswitch.  fused = 1 (the
+ * default): the inner product runs in two kernels, one over the special primes (with
+ * the row INTT of ModDown) and one over the ciphertext primes (with the end of
+ * ModDown and sigma(c0)).  fused = 0: the same arithmetic as separate launches, so
+ * that each step can be timed on its own: ModUp, the row NTT of the raised digits
+ * (CKKS_K_DIGIT_NTT), the inner product over all level+K primes into an
+ * extended-basis pair with P*sigma(c0) added on the ciphertext primes
+ * (CKKS_K_IP_EXT), then ckks_moddown's three launches on both halves.  Both give
+ * bit-identical results (the ModDown of Han and Ki, 2020, of P*sigma(c0) + acc is
+ * sigma(c0) + ModDown(acc) exactly).  The unfused route moves more data through the
+ * workspace and is slower; it processes the batch in as many groups as the
+ * workspace needs (a context of max_batch B holds 3*B*L*N words for the pairs).
+ * Affects ckks_keyswitch only (not the no-alloc, hoisted or multi-item calls).
+ * Errors: EINVAL (NULL ctx, host-only context). */
+ckks_status ckks_ctx_set_fused(ckks_ctx *ctx, uint32_t fused);
+
 /* Kernel classes of the per-kernel event timer. */
 typedef enum {
   CKKS_K_ROW = 0,          /* row pass of an NTT/INTT (1024-coefficient blocks) */
@@ -283,7 +299,10 @@ typedef enum {
   CKKS_K_RESCALE_FINAL = 9,/* row NTT fused with the rescale's subtraction and q_{l-1}^-1 */
   CKKS_K_BABY = 10,        /* baby steps of a linear transform in the extended basis */
   CKKS_K_DIAG = 11,        /* diagonal sums of a linear transform, and the sum of its giant steps */
-  CKKS_K_CLASSES = 12
+  CKKS_K_DIGIT_NTT = 12,   /* unfused key-switch: row NTT of the raised digits */
+  CKKS_K_IP_EXT = 13,      /* unfused key-switch: inner product over all level+K primes, P*sigma(c0) added */
+  CKKS_K_MODDOWN_ROW = 14, /* row INTT of the special part at the start of a standalone ModDown */
+  CKKS_K_CLASSES = 15
 } ckks_kernel_class;
 
 /* Measurement aid: while enabled, every launch of this context is bracketed by

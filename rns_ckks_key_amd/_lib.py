@@ -76,12 +76,13 @@ _SIGS = {
     "ckks_mul_relin_rescale": (ctypes.c_int, [PCTX, P, P, U32, P, ctypes.c_char_p, P, P, U32, P]),
     "ckks_ctx_set_regen_blocks": (ctypes.c_int, [PCTX, U32]),
     "ckks_ctx_set_conv_mfma": (ctypes.c_int, [PCTX, U32]),
+    "ckks_ctx_set_fused": (ctypes.c_int, [PCTX, U32]),
     "ckks_profile_enable": (ctypes.c_int, [PCTX, ctypes.c_int]),
     "ckks_profile_read": (ctypes.c_int, [PCTX, ctypes.POINTER(ctypes.c_double), PU32, U32]),
 }
 
 KERNEL_CLASSES = ["row", "col", "modup_conv", "ip_special", "moddown_conv", "ip_final", "expand", "moddown_final",
-                  "rescale_conv", "rescale_final", "baby", "diag"]
+                  "rescale_conv", "rescale_final", "baby", "diag", "digit_ntt", "ip_ext", "moddown_row"]
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

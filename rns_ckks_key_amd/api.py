@@ -107,6 +107,10 @@ class Context:
         """Base conversions on the matrix cores (True) or the vector unit (False)."""
         check(lib.ckks_ctx_set_conv_mfma(self._h, 1 if on else 0))
 
+    def set_fused(self, fused: bool) -> None:
+        """keyswitch() with the inner product fused into ModDown (True, the default) or as separate launches."""
+        check(lib.ckks_ctx_set_fused(self._h, 1 if fused else 0))
+
     def profile(self, enable: bool) -> None:
         """Bracket every launch with HIP events on its stream (measurement aid)."""
         check(lib.ckks_profile_enable(self._h, 1 if enable else 0))

@@ -314,6 +314,8 @@ struct ckks_ctx {
   const uint4* mx_md_ks = nullptr;
   const uint4* mx_md_pl = nullptr;
   bool conv_mfma = false;
+  // ckks_keyswitch with the inner product and ModDown as separate launches
+  bool unfused = false;
   // workspace (items = max_batch)
   void* ws = nullptr;
   uint64_t ws_bytes = 0;
@@ -664,7 +666,7 @@ hipError_t run_moddown(ckks_ctx* c, const uint32_t* x, uint64_t x_item, uint32_t
   r.n_limbs = h.K;
   hipError_t e;
   {
-    ProfScope p(c, CKKS_K_ROW, s);
+    ProfScope p(c, CKKS_K_MODDOWN_ROW, s);
     e = ckks::launch_row(c->d, r, false, items, s);
   }
   if (e != hipSuccess) return e;
@@ -720,12 +722,76 @@ ckks_status check_keyswitch_args(const ckks_ctx* c, const uint32_t* ct, uint32_t
   return check_keyswitch_out(c, ct, level, batch, key_b, key_a, out, (uint64_t)batch * 2 * level * c->h.n);
 }
 
+// A batched key-switch with the inner product and ModDown as separate launches (the
+// fusion knob off): ModUp, the digits' row NTT (own limbs copied from c1), the
+// extended-basis inner product with P*sigma(c0) on the ciphertext primes, and
+// ModDown of both halves.  ModUp runs once for the batch; the rest in groups of
+// items that fit the pairs buffer (tens) and ModDown's row buffer.
+ckks_status keyswitch_unfused(ckks_ctx* c, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
+                              const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt, uint32_t* out,
+                              uint32_t batch, hipStream_t s) {
+  const Host& h = c->h;
+  const uint64_t N = h.n, E = h.L + h.K, El = level + h.K, B = c->max_batch;
+  const uint64_t ext_item = (uint64_t)h.dnum * E * N;
+  const uint64_t group = std::min<uint64_t>(
+      {(uint64_t)batch, B * 3 * h.L / (2 * El), B * std::max(std::max(h.L, h.K), 2u) / (2 * h.K)});
+  if (group == 0)
+    return fail(CKKS_ERANGE, "the unfused key-switch at level %u needs a context with a larger max_batch", level);
+  hipError_t e = run_modup(c, ct + (uint64_t)level * N, 2ull * level * N, level, batch, s);
+  if (e != hipSuccess) return hip_status(e, "ModUp");
+  const uint32_t nd = digits_at(h, level);
+  for (uint32_t j = 0; j < nd; ++j) {
+    ckks::RowArgs r{};
+    r.src = r.dst = c->ext + (uint64_t)j * E * N;
+    r.src_item_stride = r.dst_item_stride = ext_item;
+    r.prime0 = 0;
+    r.n_limbs = (uint32_t)El;
+    r.own_lo = j * h.alpha;
+    r.own_n = std::min(h.alpha, level - j * h.alpha);
+    r.own_src = ct + (uint64_t)level * N;
+    r.own_item_stride = 2ull * level * N;
+    r.level = level;
+    ProfScope p(c, CKKS_K_DIGIT_NTT, s);
+    e = ckks::launch_row(c->d, r, true, batch, s);
+    if (e != hipSuccess) return hip_status(e, "digit NTT");
+  }
+  for (uint64_t i0 = 0; i0 < batch; i0 += group) {
+    const uint32_t items = (uint32_t)std::min<uint64_t>(group, batch - i0);
+    ckks::ExtArgs a{};
+    a.level = level;
+    a.nd = nd;
+    a.ext = c->ext + i0 * ext_item;
+    a.c0 = ct + i0 * 2 * level * N;
+    a.out = c->tens;
+    a.regen_blocks = c->regen_blocks;
+    a.n_keys = 1;
+    a.items = items;
+    a.ext_item = ext_item;
+    a.c0_item = 2ull * level * N;
+    a.out_item = 2 * El * N;
+    a.key[0] = ckks::KeyRef{};
+    a.key[0].b = key_b;
+    a.key[0].a = key_a;
+    if (!key_a) seed_words(key_seed, a.key[0].seed);
+    a.key[0].galois = galois_elt;
+    {
+      ProfScope p(c, CKKS_K_IP_EXT, s);
+      e = ckks::launch_rot_ext(c->d, a, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "inner product");
+    e = run_moddown(c, c->tens, El * N, level, out + i0 * 2 * level * N, (uint64_t)level * N, 2 * items, s);
+    if (e != hipSuccess) return hip_status(e, "ModDown");
+  }
+  return ok();
+}
+
 // The launch sequence of one batched key-switch, in the workspace `wsp` (the
 // context's when NULL).
 ckks_status keyswitch_run(ckks_ctx* c, const uint32_t* ct, uint32_t level, const uint32_t* key_b,
                           const uint8_t* key_seed, const uint32_t* key_a, uint32_t galois_elt, uint32_t* out,
                           uint32_t batch, hipStream_t s, const Ws* wsp) {
   const uint64_t N = c->h.n;
+  if (c->unfused && !wsp) return keyswitch_unfused(c, ct, level, key_b, key_seed, key_a, galois_elt, out, batch, s);
   const Ws w = wsp ? *wsp : ctx_ws(c);
   hipError_t e = run_modup(c, ct + (uint64_t)level * N, 2ull * level * N, level, batch, s, nullptr, nullptr, &w);
   if (e != hipSuccess) return hip_status(e, "ModUp");
@@ -864,6 +930,14 @@ ckks_status ckks_ctx_set_regen_blocks(ckks_ctx* c, uint32_t blocks) {
   if (blocks < ckks::kRow / 16 || blocks > ckks::kMaxRegenBlocks)
     return fail(CKKS_ERANGE, "regen blocks %u outside %u..%u", blocks, ckks::kRow / 16, ckks::kMaxRegenBlocks);
   c->regen_blocks = blocks;
+  return ok();
+}
+
+ckks_status ckks_ctx_set_fused(ckks_ctx* c, uint32_t fused) {
+  ckks_status st = check_ctx(c);
+  if (st) return st;
+  if (!c->max_batch) return fail(CKKS_EINVAL, "host-only context");
+  c->unfused = !fused;
   return ok();
 }
 
@@ -1174,6 +1248,7 @@ ckks_status ckks_linear_transform_bsgs(const ckks_ctx* cc, const uint32_t* ct, u
     a.out = rbuf;
     a.regen_blocks = c->regen_blocks;
     a.n_keys = n1 - 1;
+    a.items = 1;
     for (uint32_t k = 0; k + 1 < n1; ++k) {
       a.key[k] = ckks::KeyRef{};
       a.key[k].b = baby[k].key_b;

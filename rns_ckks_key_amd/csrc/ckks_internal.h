@@ -148,6 +148,10 @@ struct ExtArgs {
   uint32_t* out;             // R [key group][2][level+K][N]
   uint32_t regen_blocks;
   uint32_t n_keys;
+  // items sharing the keys: item i reads ext + i*ext_item and c0 + i*c0_item and
+  // writes out + i*out_item (a workgroup regenerates its a-tile once for all of them)
+  uint32_t items;
+  uint64_t ext_item, c0_item, out_item;
   KeyRef key[kMaxGroup];
 };
 

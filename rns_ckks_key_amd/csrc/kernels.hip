@@ -1165,10 +1165,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   ip_body<FINAL, 1, TENSOR>(T, a);
 }
 
-// Baby steps of a linear transform, in the extended basis: for key group kg and
-// limb e (prime t), R = (P*sigma(c0) + sum_j sigma(d_j)*b_j, sum_j sigma(d_j)*a_j) on
-// block blk, from hoisted digits that are already fully transformed.  One wave per
-// workgroup; a regenerated a-half lives in LDS.  Grid: x = limb, y = block, z = key.
+// Inner product in the extended basis: for key group kg and limb e (prime t),
+// R = (P*sigma(c0) + sum_j sigma(d_j)*b_j, sum_j sigma(d_j)*a_j) on block blk, from
+// digits that are already fully transformed, for each of a.items ciphertexts in turn
+// (the baby steps of a linear transform: one hoisted ciphertext, several keys; the
+// unfused key-switch: a batch, one key).  One wave per workgroup; a regenerated
+// a-half lives in LDS, built once for all items.  Grid: x = limb, y = block, z = key.
 __global__ __launch_bounds__(64) void k_rot_ext(DevTables T, ExtArgs a) {
   extern __shared__ uint32_t smem[];
   const uint32_t lane = threadIdx.x;
@@ -1200,52 +1202,56 @@ __global__ __launch_bounds__(64) void k_rot_ext(DevTables T, ExtArgs a) {
     sidx[r] = swz(galois_src(blk * kRow + rout, key.galois, T.log_n) & (kRow - 1));
   }
   const uint32_t nq = (0u - q) + opaque_zero();  // 2^32 - q, opaque: see lazy_sub_mont
-  uint32_t rb[16], ra[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { rb[r] = 0; ra[r] = 0; }
 #pragma unroll 1
-  for (uint32_t j = 0; j < nd; ++j) {
-    uint32_t x[16];
-    load_C(x, a.ext + ((uint64_t)j * E + e) * n + sblk * kRow, lane);
-    lds_put_C(priv, x, lane);
-    wave_sync();
-    const uint32_t* kb = key.b + ((uint64_t)j * E + t) * n + blk * kRow;
-    const uint32_t* ka = key.a ? key.a + ((uint64_t)j * E + t) * n + blk * kRow : Atile + j * kRow;
+  for (uint32_t item = 0; item < a.items; ++item) {
+    const uint32_t* ext = a.ext + item * a.ext_item;
+    uint32_t rb[16], ra[16];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t rout = 4 * lane + 256 * g;
-      const uint4 b4 = *reinterpret_cast<const uint4*>(kb + rout);
-      const uint4 a4 = *reinterpret_cast<const uint4*>(ka + rout);
-      const uint32_t bv[4] = {b4.x, b4.y, b4.z, b4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+    for (int r = 0; r < 16; ++r) { rb[r] = 0; ra[r] = 0; }
+#pragma unroll 1
+    for (uint32_t j = 0; j < nd; ++j) {
+      uint32_t x[16];
+      load_C(x, ext + ((uint64_t)j * E + e) * n + sblk * kRow, lane);
+      lds_put_C(priv, x, lane);
+      wave_sync();
+      const uint32_t* kb = key.b + ((uint64_t)j * E + t) * n + blk * kRow;
+      const uint32_t* ka = key.a ? key.a + ((uint64_t)j * E + t) * n + blk * kRow : Atile + j * kRow;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 4 * g + v;
-        const uint32_t d = priv[sidx[r]];
-        rb[r] = lazy_add_mont(rb[r], d, bv[v], md, nq);  // lazy: only multiplied afterwards
-        ra[r] = lazy_add_mont(ra[r], d, av[v], md, nq);
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t rout = 4 * lane + 256 * g;
+        const uint4 b4 = *reinterpret_cast<const uint4*>(kb + rout);
+        const uint4 a4 = *reinterpret_cast<const uint4*>(ka + rout);
+        const uint32_t bv[4] = {b4.x, b4.y, b4.z, b4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * g + v;
+          const uint32_t d = priv[sidx[r]];
+          rb[r] = lazy_add_mont(rb[r], d, bv[v], md, nq);  // lazy: only multiplied afterwards
+          ra[r] = lazy_add_mont(ra[r], d, av[v], md, nq);
+        }
       }
+      wave_sync();
     }
-    wave_sync();
-  }
-  const uint2 r2 = T.r2[t];  // the Montgomery products carry 2^-32
+    const uint2 r2 = T.r2[t];  // the Montgomery products carry 2^-32
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    rb[r] = mul_const(rb[r], r2.x, r2.y, q);
-    ra[r] = mul_const(ra[r], r2.x, r2.y, q);
-  }
-  if (e < level) {  // + P*sigma(c0) on the ciphertext primes
-    uint32_t c[16];
-    load_C(c, a.c0 + (uint64_t)e * n + sblk * kRow, lane);
-    lds_put_C(priv, c, lane);
-    wave_sync();
-    const uint2 pm = T.p_mod[e];
+    for (int r = 0; r < 16; ++r) {
+      rb[r] = mul_const(rb[r], r2.x, r2.y, q);
+      ra[r] = mul_const(ra[r], r2.x, r2.y, q);
+    }
+    if (e < level) {  // + P*sigma(c0) on the ciphertext primes
+      uint32_t c[16];
+      load_C(c, a.c0 + item * a.c0_item + (uint64_t)e * n + sblk * kRow, lane);
+      lds_put_C(priv, c, lane);
+      wave_sync();
+      const uint2 pm = T.p_mod[e];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rb[r] = add_mod(rb[r], mul_const(priv[sidx[r]], pm.x, pm.y, q), q);
-    wave_sync();
+      for (int r = 0; r < 16; ++r) rb[r] = add_mod(rb[r], mul_const(priv[sidx[r]], pm.x, pm.y, q), q);
+      wave_sync();
+    }
+    uint32_t* out = a.out + item * a.out_item + (uint64_t)kg * 2 * El * n + (uint64_t)e * n + blk * kRow;
+    store_C(out, rb, lane);
+    store_C(out + (uint64_t)El * n, ra, lane);
   }
-  uint32_t* out = a.out + (uint64_t)kg * 2 * El * n + (uint64_t)e * n + blk * kRow;
-  store_C(out, rb, lane);
-  store_C(out + (uint64_t)El * n, ra, lane);
 }
 
 // S_j = sum_k D[j][k] * R_k for every giant step j, on 4 coefficients per thread of

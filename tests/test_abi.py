@@ -202,6 +202,14 @@ def test_conv_mfma_switch_validates_the_shape():
     assert lib.ckks_ctx_set_conv_mfma(None, 1) == EINVAL
 
 
+def test_fusion_switch_needs_a_device_context():
+    host = Context.for_chain(12, 4, 2, 2, 30, max_batch=0)
+    assert lib.ckks_ctx_set_fused(host.handle, 0) == EINVAL  # host-only: there is no call to reroute
+    assert "host-only" in lib.ckks_last_error().decode()
+    host.close()
+    assert lib.ckks_ctx_set_fused(None, 1) == EINVAL
+
+
 def test_noalloc_keyswitch_validates_before_any_launch():
     # ckks_keyswitch_noalloc: the key-switch's checks, then its batch against the static
     # scratch array (96 MiB per GPU), not against max_batch
