@@ -45,7 +45,7 @@ ROTATE = 4
 
 # ---------------------------------------------------------------- work model
 # Algorithmic work in 32-bit VALU lane-op slots (one full-rate op on one lane):
-# the per-unit costs of the survey's model with full-rate 32-bit multiplies
+# per-unit costs that assume full-rate 32-bit multiplies
 # (measured on gfx950): a butterfly is one Montgomery constant multiply (3
 # multiplies + 3 adds) plus a modular add and a modular subtract; a MAC is a
 # 32x32->64 product accumulated into 96 bits; a reduction is the two-word REDC;
