@@ -26,6 +26,7 @@
 // sums over sources as int8 matrix-core products (selected per context).  A
 // relinearisation never stores its tensor product: the inverse row pass forms
 // x1*y1 (k_row MUL) and the final inner-product pass the other products (TENSOR).
+#include <type_traits>
 #include <utility>
 
 #include "ckks_internal.h"
@@ -90,8 +91,8 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return r + ((r >> 6) << 2)
 // (t = b*w is canonical, so a + t and a - t each take one carry-selected
 // correction); otherwise all are canonical.
 template <bool LAZY = true>
-__device__ __forceinline__ void ct_bfly(uint32_t& a, uint32_t& b, uint32_t w, uint32_t qinv, uint32_t q) {
-  const uint32_t t = mul_const(b, w, w * qinv, q);
+__device__ __forceinline__ void ct_bfly_c(uint32_t& a, uint32_t& b, uint2 w, uint32_t q) {
+  const uint32_t t = mul_const(b, w.x, w.y, q);
   if constexpr (LAZY) {
     b = lazy_sub(a, t, q);
     a = lazy_add(a, t, q);
@@ -99,6 +100,10 @@ __device__ __forceinline__ void ct_bfly(uint32_t& a, uint32_t& b, uint32_t w, ui
     b = sub_mod(a, t, q);
     a = add_mod(a, t, q);
   }
+}
+template <bool LAZY = true>
+__device__ __forceinline__ void ct_bfly(uint32_t& a, uint32_t& b, uint32_t w, uint32_t qinv, uint32_t q) {
+  ct_bfly_c<LAZY>(a, b, make_uint2(w, w * qinv), q);
 }
 
 // Canonical residues of lazy values for q > 2^31 (x < 2q): min(x, x - q).
@@ -116,12 +121,24 @@ __device__ __forceinline__ uint32_t prod_mod(uint32_t a, uint32_t b, const Mod& 
   return mul_const(mont_mul(a, b, md), r2.x, r2.y, md.q);
 }
 
-__device__ __forceinline__ void gs_bfly(uint32_t& a, uint32_t& b, uint32_t w, uint32_t qinv, uint32_t q) {
+__device__ __forceinline__ void gs_bfly_c(uint32_t& a, uint32_t& b, uint2 w, uint32_t q) {
   uint32_t s = add_mod(a, b, q);
   uint32_t d = sub_mod(a, b, q);
   a = s;
-  b = mul_const(d, w, w * qinv, q);
+  b = mul_const(d, w.x, w.y, q);
 }
+__device__ __forceinline__ void gs_bfly(uint32_t& a, uint32_t& b, uint32_t w, uint32_t qinv, uint32_t q) {
+  gs_bfly_c(a, b, make_uint2(w, w * qinv), q);
+}
+
+// Twiddle i of a row transform with its Montgomery companion: from a limb's table of
+// w*2^32 mod q (companion computed, on the scalar unit when i is wave-uniform), or
+// from a block's staged copy that holds both.
+__device__ __forceinline__ uint2 twc(const uint32_t* __restrict__ tw, uint32_t i, uint32_t qinv) {
+  const uint32_t w = tw[i];
+  return make_uint2(w, w * qinv);
+}
+__device__ __forceinline__ uint2 twc(const uint2* __restrict__ tw, uint32_t i, uint32_t) { return tw[i]; }
 
 __device__ __forceinline__ void load_A(uint32_t (&x)[16], const uint32_t* __restrict__ p, uint32_t lane) {
 #pragma unroll
@@ -187,8 +204,8 @@ __device__ __forceinline__ void lds_get_B(uint32_t (&x)[16], const uint32_t* lds
 // lazy values; CANON makes the outputs canonical (callers that only multiply them
 // by constants skip it).  BIG: the prime exceeds 2^31, known at compile time, so
 // canonical is one conditional subtraction with no branch on q.
-template <bool CANON = true, bool BIG = false>
-__device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32_t off, const uint32_t* __restrict__ tw,
+template <bool CANON = true, bool BIG = false, class Tw>
+__device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32_t off, const Tw* __restrict__ tw,
                                         uint32_t q, uint32_t qinv, uint32_t* lds, uint2 one) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -196,9 +213,9 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
     const uint32_t m = 1u << s;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = tw[m * off + grp];
+      const uint2 w = twc(tw, m * off + grp, qinv);
 #pragma unroll
-      for (int kk = 0; kk < h; ++kk) ct_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
+      for (int kk = 0; kk < h; ++kk) ct_bfly_c(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, q);
     }
   }
   lds_put_A(lds, x, lane);
@@ -213,9 +230,9 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
     const uint32_t base = m * off + 8 * hb / h;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = tw[base + grp];
+      const uint2 w = twc(tw, base + grp, qinv);
 #pragma unroll
-      for (int kk = 0; kk < h; ++kk) ct_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
+      for (int kk = 0; kk < h; ++kk) ct_bfly_c(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, q);
     }
   }
   lds_put_B(lds, x, lane);
@@ -224,13 +241,13 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
   wave_sync();
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const uint32_t w = tw[256 * off + lane + 64 * g];
-    ct_bfly(x[4 * g], x[4 * g + 2], w, qinv, q);
-    ct_bfly(x[4 * g + 1], x[4 * g + 3], w, qinv, q);
+    const uint2 w = twc(tw, 256 * off + lane + 64 * g, qinv);
+    ct_bfly_c(x[4 * g], x[4 * g + 2], w, q);
+    ct_bfly_c(x[4 * g + 1], x[4 * g + 3], w, q);
     const uint32_t i1 = 512 * off + 2 * lane + 128 * g;
-    const uint32_t w0 = tw[i1], w1 = tw[i1 + 1];
-    ct_bfly(x[4 * g], x[4 * g + 1], w0, qinv, q);
-    ct_bfly(x[4 * g + 2], x[4 * g + 3], w1, qinv, q);
+    const uint2 w0 = twc(tw, i1, qinv), w1 = twc(tw, i1 + 1, qinv);
+    ct_bfly_c(x[4 * g], x[4 * g + 1], w0, q);
+    ct_bfly_c(x[4 * g + 2], x[4 * g + 3], w1, q);
   }
   if constexpr (CANON && BIG) {
     canon_big(x, q);
@@ -242,17 +259,18 @@ __device__ __forceinline__ void row_fwd(uint32_t (&x)[16], uint32_t lane, uint32
 
 // Inverse stages 1..512 of one 1024-block: layout C in, layout A out (no N^-1).
 // Twiddles indexed as in row_fwd (off = N/1024 + blk, or 1 with a block's copy).
-__device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32_t off, const uint32_t* __restrict__ itw,
+template <class Tw>
+__device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32_t off, const Tw* __restrict__ itw,
                                         uint32_t q, uint32_t qinv, uint32_t* lds) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint32_t i1 = 512 * off + 2 * lane + 128 * g;
-    const uint32_t w0 = itw[i1], w1 = itw[i1 + 1];
-    gs_bfly(x[4 * g], x[4 * g + 1], w0, qinv, q);
-    gs_bfly(x[4 * g + 2], x[4 * g + 3], w1, qinv, q);
-    const uint32_t w = itw[256 * off + lane + 64 * g];
-    gs_bfly(x[4 * g], x[4 * g + 2], w, qinv, q);
-    gs_bfly(x[4 * g + 1], x[4 * g + 3], w, qinv, q);
+    const uint2 w0 = twc(itw, i1, qinv), w1 = twc(itw, i1 + 1, qinv);
+    gs_bfly_c(x[4 * g], x[4 * g + 1], w0, q);
+    gs_bfly_c(x[4 * g + 2], x[4 * g + 3], w1, q);
+    const uint2 w = twc(itw, 256 * off + lane + 64 * g, qinv);
+    gs_bfly_c(x[4 * g], x[4 * g + 2], w, q);
+    gs_bfly_c(x[4 * g + 1], x[4 * g + 3], w, q);
   }
   lds_put_C(lds, x, lane);
   wave_sync();
@@ -266,9 +284,9 @@ __device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32
     const uint32_t base = m * off + 8 * hb / h;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = itw[base + grp];
+      const uint2 w = twc(itw, base + grp, qinv);
 #pragma unroll
-      for (int kk = 0; kk < h; ++kk) gs_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
+      for (int kk = 0; kk < h; ++kk) gs_bfly_c(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, q);
     }
   }
   lds_put_B(lds, x, lane);
@@ -281,9 +299,9 @@ __device__ __forceinline__ void row_inv(uint32_t (&x)[16], uint32_t lane, uint32
     const uint32_t m = 8u >> s;
 #pragma unroll
     for (int grp = 0; grp < 8 / h; ++grp) {
-      const uint32_t w = itw[m * off + grp];
+      const uint2 w = twc(itw, m * off + grp, qinv);
 #pragma unroll
-      for (int kk = 0; kk < h; ++kk) gs_bfly(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, qinv, q);
+      for (int kk = 0; kk < h; ++kk) gs_bfly_c(x[2 * grp * h + kk], x[2 * grp * h + kk + h], w, q);
     }
   }
 }
@@ -295,6 +313,15 @@ __device__ __forceinline__ void stage_block_twiddles(uint32_t* dst, const uint32
   for (uint32_t k = threadIdx.x + 1; k < kRow; k += blockDim.x) {
     const uint32_t m = 1u << (31 - __builtin_clz(k));  // the stage of entry k: m <= k < 2m
     dst[k] = tw[m * off + (k - m)];
+  }
+}
+// The same copy with each twiddle's Montgomery companion beside it.
+__device__ __forceinline__ void stage_block_twiddles(uint2* dst, const uint32_t* __restrict__ tw, uint32_t off,
+                                                     uint32_t qinv) {
+  for (uint32_t k = threadIdx.x + 1; k < kRow; k += blockDim.x) {
+    const uint32_t m = 1u << (31 - __builtin_clz(k));
+    const uint32_t w = tw[m * off + (k - m)];
+    dst[k] = make_uint2(w, w * qinv);
   }
 }
 
@@ -333,6 +360,35 @@ __device__ __forceinline__ void col_inv(uint32_t (&v)[1 << LOGC], const uint32_t
 #pragma unroll
       for (int k = 0; k < h; ++k) gs_bfly(v[2 * i * h + k], v[2 * i * h + k + h], w, qinv, q);
     }
+  }
+}
+
+// col_inv, then every output times the constant sc (w*2^32 mod q, companion), with
+// that multiplication folded into the last stage: its sums are multiplied by sc and
+// its differences by w*sc (w the stage's one twiddle), instead of the differences by
+// w and then all outputs by sc.  The results are the same residues, canonical.
+template <int LOGC>
+__device__ __forceinline__ void col_inv_scaled(uint32_t (&v)[1 << LOGC], const uint32_t* __restrict__ itw,
+                                               uint32_t q, uint32_t qinv, uint2 sc) {
+  constexpr int C = 1 << LOGC;
+#pragma unroll
+  for (int s = LOGC - 1; s >= 1; --s) {
+    const int m = 1 << s;
+    const int h = C >> (s + 1);
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      const uint32_t w = itw[m + i];
+#pragma unroll
+      for (int k = 0; k < h; ++k) gs_bfly(v[2 * i * h + k], v[2 * i * h + k + h], w, qinv, q);
+    }
+  }
+  const uint32_t wsc = mont_mul(itw[1], sc.x, Mod{q, qinv});  // (w * scale) in Montgomery form
+  const uint32_t wscq = wsc * qinv;
+#pragma unroll
+  for (int k = 0; k < C / 2; ++k) {
+    const uint32_t a = v[k], b = v[k + C / 2];  // canonical: outputs of the stages above
+    v[k] = mul_const(lazy_add(a, b, q), sc.x, sc.y, q);
+    v[k + C / 2] = mul_const(lazy_sub(a, b, q), wsc, wscq, q);
   }
 }
 
@@ -564,8 +620,10 @@ __global__ __launch_bounds__(64) void k_col(DevTables T, ColArgs a, uint32_t sca
   } else if constexpr (FWD) {
     col_fwd<LOGC, false>(v, T.tw + (uint64_t)tp * n, q, T.qinv[tp]);
   }
-  if constexpr (!FWD) col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
-  if (scale) {
+  if constexpr (!FWD) {
+    if (scale) col_inv_scaled<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp], T.ninv[tp]);
+    else col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
+  } else if (scale) {
     const uint2 s = T.ninv[tp];
 #pragma unroll
     for (int k = 0; k < C; ++k) v[k] = mul_const(v[k], s.x, s.y, q);
@@ -746,10 +804,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const uint32_t* ps = src + (uint64_t)s * n + col0 + c;
 #pragma unroll
     for (int k = 0; k < C; ++k) v[k] = ps[k * kRow];
-    col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
-    const uint2 sc = a.scale[y * a.scale_y + s];
+    col_inv_scaled<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp], a.scale[y * a.scale_y + s]);
 #pragma unroll
-    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = mul_const(v[k], sc.x, sc.y, q);
+    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = v[k];
     if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
   }
   __syncthreads();
@@ -840,10 +897,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const uint32_t* ps = src + (uint64_t)s * n + col0 + c;
 #pragma unroll
     for (int k = 0; k < C; ++k) v[k] = ps[k * kRow];
-    col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
-    const uint2 sc = a.scale[y * a.scale_y + s];
+    col_inv_scaled<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp], a.scale[y * a.scale_y + s]);
 #pragma unroll
-    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = mul_const(v[k], sc.x, sc.y, q);
+    for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = v[k];
   }
   __syncthreads();
   // B operands: the digits of this wave's eight coefficient tiles (sources past ns hold
@@ -968,11 +1024,16 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
   // Several waves also share the twiddles of this prime's blocks: the final pass's
   // conv transform uses block blk, the digits' transforms block sblk (their source
   // under sigma_g), the special pass's inverse transform block blk.  Staged in LDS
-  // (two tables of 1024 words), they replace per-lane loads from the limb's table
-  // in the middle of each transform.
-  uint32_t* twA = smem + tile_words;                        // sblk's forward twiddles (staged only)
-  uint32_t* twB = twA + kRow;                               // blk's forward (FINAL) or inverse twiddles
-  const uint32_t stw = kStage ? 2 * kRow : 0u;
+  // (two tables of 1024 entries), they replace per-lane loads from the limb's table
+  // in the middle of each transform.  With eight waves each entry also carries its
+  // Montgomery companion (8 KB a table), which saves the transforms a multiply per
+  // twiddle; the four-wave kernel keeps 4 KB tables, so that three of its workgroups
+  // still fit a CU.
+  constexpr bool kTwc = WAVES == 8;
+  using TwT = std::conditional_t<kTwc, uint2, uint32_t>;
+  TwT* twA = reinterpret_cast<TwT*>(smem + tile_words);     // sblk's forward twiddles (staged only)
+  TwT* twB = twA + kRow;                                    // blk's forward (FINAL) or inverse twiddles
+  const uint32_t stw = kStage ? (kTwc ? 4 : 2) * kRow : 0u;
   uint32_t* priv = smem + tile_words + stw + wave * kRowPad;  // wave-private block
   uint32_t* cnt = smem + tile_words + stw + WAVES * kRowPad;  // expander scratch
   const uint32_t sblk = galois_src(blk * kRow, key.galois, T.log_n) >> 10;
@@ -984,8 +1045,13 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
       *reinterpret_cast<uint4*>(Btile + j * kRow + 4 * w4) = *reinterpret_cast<const uint4*>(key.b + off);
       if (key.a) *reinterpret_cast<uint4*>(Atile + j * kRow + 4 * w4) = *reinterpret_cast<const uint4*>(key.a + off);
     }
-    stage_block_twiddles(twA, tw, n / kRow + sblk);
-    stage_block_twiddles(twB, FINAL ? tw : T.itw + (uint64_t)tabs * n, n / kRow + blk);
+    if constexpr (kTwc) {
+      stage_block_twiddles(twA, tw, n / kRow + sblk, md.qinv);
+      stage_block_twiddles(twB, FINAL ? tw : T.itw + (uint64_t)tabs * n, n / kRow + blk, md.qinv);
+    } else {
+      stage_block_twiddles(twA, tw, n / kRow + sblk);
+      stage_block_twiddles(twB, FINAL ? tw : T.itw + (uint64_t)tabs * n, n / kRow + blk);
+    }
   }
   if (!key.a) {
     uint32_t seed[8];
@@ -994,10 +1060,19 @@ __device__ __forceinline__ void ip_body(const DevTables& T, const IpArgs& a) {
   }
   __syncthreads();
   // twiddle sources and offsets of the three kinds of row transform
-  const uint32_t* tw_dig = kStage ? twA : tw;
-  const uint32_t off_dig = kStage ? 1u : n / kRow + sblk;
-  const uint32_t* tw_blk = kStage ? twB : (FINAL ? tw : T.itw + (uint64_t)tabs * n);
-  const uint32_t off_blk = kStage ? 1u : n / kRow + blk;
+  const TwT* tw_dig;
+  const TwT* tw_blk;
+  uint32_t off_dig, off_blk;
+  if constexpr (kStage) {
+    tw_dig = twA;
+    tw_blk = twB;
+    off_dig = off_blk = 1u;
+  } else {
+    tw_dig = tw;
+    tw_blk = FINAL ? tw : T.itw + (uint64_t)tabs * n;
+    off_dig = n / kRow + sblk;
+    off_blk = n / kRow + blk;
+  }
   const uint32_t* kb_row = kStage ? Btile : key.b + (uint64_t)tabs * n + blk * kRow;
   const uint32_t* ka_row = a_in_lds ? Atile : key.a + (uint64_t)tabs * n + blk * kRow;
   const uint64_t bstride = kStage ? kRow : (uint64_t)E * n;   // digit stride of kb_row
@@ -1486,7 +1561,9 @@ hipError_t launch_ip(const DevTables& T, const IpArgs& a, bool final_pass, uint3
   bool regen = false;
   for (uint32_t k = 0; k < a.n_keys; ++k) regen |= a.key[k].a == nullptr;
   // staged key rows and two block twiddle tables (multi-wave), or a regenerated a-half
-  const size_t tiles = (waves > 1 ? 2 * ((size_t)a.nd + 1) * kRow : (regen ? (size_t)a.nd * kRow : 0));
+  // (the eight-wave kernels' twiddle tables hold companions too: 2 words an entry)
+  const size_t tw_words = waves == 8 ? 4 * kRow : 2 * kRow;
+  const size_t tiles = (waves > 1 ? 2 * (size_t)a.nd * kRow + tw_words : (regen ? (size_t)a.nd * kRow : 0));
   const size_t shm = (tiles + waves * kRowPad + (regen ? 2 * a.nd + 16 + 64 : 0)) * sizeof(uint32_t);
   const bool big = T.all_big;  // the multi-wave final passes canonicalise conv's transform without a branch on q
   if (final_pass) {
