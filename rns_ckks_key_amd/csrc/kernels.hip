@@ -620,10 +620,8 @@ __global__ __launch_bounds__(64) void k_col(DevTables T, ColArgs a, uint32_t sca
   } else if constexpr (FWD) {
     col_fwd<LOGC, false>(v, T.tw + (uint64_t)tp * n, q, T.qinv[tp]);
   }
-  if constexpr (!FWD) {
-    if (scale) col_inv_scaled<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp], T.ninv[tp]);
-    else col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
-  } else if (scale) {
+  if constexpr (!FWD) col_inv<LOGC>(v, T.itw + (uint64_t)tp * n, q, T.qinv[tp]);
+  if (scale) {
     const uint2 s = T.ninv[tp];
 #pragma unroll
     for (int k = 0; k < C; ++k) v[k] = mul_const(v[k], s.x, s.y, q);
