@@ -794,6 +794,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (task1 >= ns * CW) {
     if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
   } else {
+    __builtin_amdgcn_s_setprio(2);  // the rest of the workgroup waits for phase 1
     const uint32_t task = task1;
     const uint32_t s = task / CW, c = task - s * CW;
     const uint32_t tp = p0 + s;
@@ -806,6 +807,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 #pragma unroll
     for (int k = 0; k < C; ++k) ys[(k * CW + c) * MAXS + s] = v[k];
     if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   uint32_t* dst = a.dst + item * a.dst_item + y * a.dst_y;
