@@ -102,11 +102,23 @@ def hbm_bytes(level: int, batch: int, regen: bool, n_keys: int = 1) -> float:
 
 # ---------------------------------------------------------------- committed counter summaries
 
-def kernel_source_hash() -> str:
+def code_text(src: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the compiler sees."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(texts: list[str] | None = None) -> str:
+    """Hash of the device sources' code (comments and layout ignored), first 16 hex digits."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "modarith.h", "ckks_internal.h"):
-        with open(os.path.join(ROOT, "rns_ckks_key_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for i, f in enumerate(("kernels.hip", "modarith.h", "ckks_internal.h")):
+        if texts is None:
+            with open(os.path.join(ROOT, "rns_ckks_key_amd", "csrc", f)) as fh:
+                src = fh.read()
+        else:
+            src = texts[i]
+        h.update(code_text(src).encode())
     return h.hexdigest()[:16]
 
 

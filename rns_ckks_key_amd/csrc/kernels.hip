@@ -794,7 +794,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (task1 >= ns * CW) {
     if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
   } else {
-    __builtin_amdgcn_s_setprio(2);  // the rest of the workgroup waits for phase 1
+    // The rest of the workgroup waits at the barrier for these waves, while the other
+    // workgroup on the CU competes for the SIMDs: raise their issue priority meanwhile.
+    __builtin_amdgcn_s_setprio(2);
     const uint32_t task = task1;
     const uint32_t s = task / CW, c = task - s * CW;
     const uint32_t tp = p0 + s;

@@ -98,3 +98,14 @@ def test_instruction_rates_parse():
     rates = bench.read_valu_rates()
     assert rates is not None
     assert 30 < rates["v_mul_lo_u32"] < 45 and 55 < rates["v_add_u32"] < 75
+
+
+def test_source_hash_follows_code_not_comments():
+    paths = [os.path.join(ROOT, "rns_ckks_key_amd", "csrc", f) for f in ("kernels.hip", "modarith.h", "ckks_internal.h")]
+    texts = [open(p).read() for p in paths]
+    h = bench.kernel_source_hash(texts)
+    assert h == bench.kernel_source_hash()
+    commented = ["// a note\n" + texts[0].replace("\n", "  \n", 3) + "/* more */", texts[1], texts[2]]
+    assert bench.kernel_source_hash(commented) == h
+    changed = [texts[0] + "\nstatic int extra_symbol;", texts[1], texts[2]]
+    assert bench.kernel_source_hash(changed) != h
