@@ -368,8 +368,9 @@ def headline(args, primes, torch):
     dominant = max(per_call, key=per_call.get)
     t_dom = per_launch[dominant] * 1e-3
     achieved = wm[dominant] / t_dom
-    traffic = read_traffic(dominant)
-    issue = read_issue(dominant)
+    # the committed counter summaries were taken on the vector-unit conversion
+    traffic = read_traffic(dominant) if args.conv == "vector" else None
+    issue = read_issue(dominant) if args.conv == "vector" else None
     rates = read_valu_rates()
     total_slots = sum(wm.values())
     t_call = head_ms * 1e-3
