@@ -392,6 +392,37 @@ __device__ __forceinline__ void col_inv_scaled(uint32_t (&v)[1 << LOGC], const u
   }
 }
 
+// col_inv_scaled on two lanes per column: lane z of an aligned lane pair holds rows
+// z*C/2 .. z*C/2 + C/2 - 1.  Every stage but the last stays in the lane (the lane's
+// half of the column holds whole butterfly groups); the last pairs the two lanes, the
+// sums landing in lane 0 (times sc) and the differences in lane 1 (times w*sc).
+template <int LOGC>
+__device__ __forceinline__ void col_inv_scaled_pair(uint32_t (&v)[(1 << LOGC) / 2], uint32_t z,
+                                                    const uint32_t* __restrict__ itw, uint32_t q, uint32_t qinv,
+                                                    uint2 sc) {
+  constexpr int C = 1 << LOGC, H = C / 2;
+#pragma unroll
+  for (int s = LOGC - 1; s >= 1; --s) {
+    const int m = 1 << s;
+    const int h = C >> (s + 1);
+#pragma unroll
+    for (int i = 0; i < m / 2; ++i) {
+      const uint32_t w = itw[m + z * (m / 2) + i];
+#pragma unroll
+      for (int k = 0; k < h; ++k) gs_bfly(v[2 * i * h + k], v[2 * i * h + k + h], w, qinv, q);
+    }
+  }
+  const uint32_t wsc = mont_mul(itw[1], sc.x, Mod{q, qinv});
+  const uint32_t cx = z ? wsc : sc.x, cy = z ? wsc * qinv : sc.y;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const uint32_t own = v[k];
+    const uint32_t other = __builtin_amdgcn_mov_dpp(own, 0xB1, 0xf, 0xf, true);  // the pair's other lane
+    const uint32_t sum = lazy_add(own, other, q), dif = lazy_sub(other, own, q);
+    v[k] = mul_const(z ? dif : sum, cx, cy, q);
+  }
+}
+
 // ------------------------------------------------------------------ ChaCha12
 
 // ChaCha block function (Bernstein 2008) with 12 rounds: state = constant
@@ -791,8 +822,26 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const bool has_first = threadIdx.x < nfirst;
   ConvTarget<MAXS> first;
   const uint32_t task1 = threadIdx.x;
-  if (task1 >= ns * CW) {
+  // two lanes per (source, column) when the workgroup has the threads for it
+  const bool pair = 2 * ns * CW <= nth;
+  if (task1 >= (pair ? 2 : 1) * ns * CW) {
     if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
+  } else if (pair) {
+    __builtin_amdgcn_s_setprio(2);
+    const uint32_t pt = task1 >> 1, z = task1 & 1;
+    const uint32_t s = pt / CW, c = pt - s * CW;
+    const uint32_t tp = p0 + s;
+    const uint32_t q = T.q[tp];
+    constexpr int H = C / 2;
+    uint32_t v[H];
+    const uint32_t* ps = src + (uint64_t)s * n + col0 + c + (uint64_t)z * H * kRow;
+#pragma unroll
+    for (int k = 0; k < H; ++k) v[k] = ps[k * kRow];
+    col_inv_scaled_pair<LOGC>(v, z, T.itw + (uint64_t)tp * n, q, T.qinv[tp], a.scale[y * a.scale_y + s]);
+#pragma unroll
+    for (int k = 0; k < H; ++k) ys[((z * H + k) * CW + c) * MAXS + s] = v[k];
+    if (has_first) first = conv_target<MAXS>(T, a, e0 + threadIdx.x / CW, ns, skip_lo, y);
+    __builtin_amdgcn_s_setprio(0);
   } else {
     // The rest of the workgroup waits at the barrier for these waves, while the other
     // workgroup on the CU competes for the SIMDs: raise their issue priority meanwhile.
