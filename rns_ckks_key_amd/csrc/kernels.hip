@@ -79,11 +79,19 @@ __device__ __forceinline__ uint32_t xcd_logical_id() {
 }
 
 // LDS position of coefficient r of a 1024-word block: 4 pad words after every
-// 64.  Affine in the unrolled register index for every layout (so LDS
-// instructions use immediate offsets), 16-byte aligned for layout C, and free
-// of bank conflicts within each half-wave for layouts A, B and C.
+// 64.  16-byte aligned for layout C, and free of bank conflicts within each
+// half-wave for layouts A, B and C.  For a lane below 64 the position of each
+// layout's register k is a per-lane base plus a constant (the pad count depends
+// on k and the lane's high bits only), written out below so that every LDS
+// instruction takes an immediate offset even where the lane index is opaque to
+// the compiler:
+//   A: r = lane + 64k              -> lane + 68k
+//   B: r = 64(lane/4) + lane%4 + 4k -> 68(lane/4) + lane%4 + 4k
+//   C: r = 4 lane + 256g           -> 4 lane + 4(lane/16) + 272g
 constexpr uint32_t kRowPad = kRow + kRow / 16;
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return r + ((r >> 6) << 2); }
+__device__ __forceinline__ uint32_t lds_base_B(uint32_t lane) { return 68 * (lane >> 2) + (lane & 3); }
+__device__ __forceinline__ uint32_t lds_base_C(uint32_t lane) { return 4 * lane + 4 * (lane >> 4); }
 
 // Twiddles are stored as w*2^32 mod q only; the Montgomery companion w*q^-1 mod 2^32
 // is one multiply (a scalar one when the twiddle is wave-uniform).
@@ -164,34 +172,38 @@ __device__ __forceinline__ void store_C(uint32_t* __restrict__ p, const uint32_t
 }
 // layout C registers -> LDS block in natural (swizzled) order, and back
 __device__ __forceinline__ void lds_put_C(uint32_t* lds, const uint32_t (&x)[16], uint32_t lane) {
+  uint32_t* p = lds + lds_base_C(lane);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
-    *reinterpret_cast<uint4*>(lds + swz(4 * lane + 256 * g)) = make_uint4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+    *reinterpret_cast<uint4*>(p + 272 * g) = make_uint4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
 }
 __device__ __forceinline__ void lds_get_C(uint32_t (&x)[16], const uint32_t* lds, uint32_t lane) {
+  const uint32_t* p = lds + lds_base_C(lane);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    uint4 v = *reinterpret_cast<const uint4*>(lds + swz(4 * lane + 256 * g));
+    uint4 v = *reinterpret_cast<const uint4*>(p + 272 * g);
     x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
   }
 }
 __device__ __forceinline__ void lds_put_A(uint32_t* lds, const uint32_t (&x)[16], uint32_t lane) {
+  uint32_t* p = lds + lane;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) lds[swz(lane + 64 * k)] = x[k];
+  for (int k = 0; k < 16; ++k) p[68 * k] = x[k];
 }
 __device__ __forceinline__ void lds_get_A(uint32_t (&x)[16], const uint32_t* lds, uint32_t lane) {
+  const uint32_t* p = lds + lane;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) x[k] = lds[swz(lane + 64 * k)];
+  for (int k = 0; k < 16; ++k) x[k] = p[68 * k];
 }
 __device__ __forceinline__ void lds_put_B(uint32_t* lds, const uint32_t (&x)[16], uint32_t lane) {
-  const uint32_t base = 64 * (lane >> 2) + (lane & 3);
+  uint32_t* p = lds + lds_base_B(lane);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) lds[swz(base + 4 * k)] = x[k];
+  for (int k = 0; k < 16; ++k) p[4 * k] = x[k];
 }
 __device__ __forceinline__ void lds_get_B(uint32_t (&x)[16], const uint32_t* lds, uint32_t lane) {
-  const uint32_t base = 64 * (lane >> 2) + (lane & 3);
+  const uint32_t* p = lds + lds_base_B(lane);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) x[k] = lds[swz(base + 4 * k)];
+  for (int k = 0; k < 16; ++k) x[k] = p[4 * k];
 }
 
 // ------------------------------------------------------------------ row pass
