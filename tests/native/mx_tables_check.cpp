@@ -1,7 +1,8 @@
 // Host check of the matrix-core conversion's operand tables (no GPU).
 //
-// The library's host code is compiled in (api.cpp, launchers and the no-alloc scratch stubbed out).  For the
-// N = 2^16, 36 + 12 prime chain it builds the tables, then emulates what the
+// The library's host code is compiled in (api.cpp; the launchers and the no-alloc
+// scratch are stubbed out by launch_stubs.h).  For the N = 2^16, 36 + 12 prime
+// chain it builds the tables, then emulates what the
 // conversion kernel computes from them: the int8 product of a constant tile (A) and
 // the 7-bit digits of 32 coefficients' source values (B), in the lane layout of
 // v_mfma_i32_32x32x32_i8 (lane l holds row l % 32 of A and column l % 32 of B with
@@ -17,28 +18,7 @@
 #include <cstdio>
 #include <random>
 
-namespace ckks {
-hipError_t launch_row(const DevTables&, const RowArgs&, bool, uint32_t, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_col(const DevTables&, const ColArgs&, bool, bool, uint32_t, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-hipError_t launch_conv(const DevTables&, const ConvArgs&, uint32_t, uint32_t, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-hipError_t launch_ip(const DevTables&, const IpArgs&, bool, uint32_t, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_rot_ext(const DevTables&, const ExtArgs&, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_diag_acc(const DevTables&, const DiagArgs&, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_sum(const DevTables&, const SumArgs&, uint32_t*, uint32_t, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-hipError_t launch_expand(const DevTables&, const uint32_t*, uint32_t*, uint32_t, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-// the no-alloc key-switch's static array lives in device code, not compiled here
-hipError_t scratch_setup(int) { return hipErrorInvalidValue; }
-uint32_t* scratch_ptr(int) { return nullptr; }
-const char* scratch_error(int) { return "not built into the host check"; }
-}  // namespace ckks
+#include "launch_stubs.h"
 
 namespace {
 
