@@ -156,9 +156,30 @@ def read_valu_rates() -> dict | None:
     if not os.path.exists(path):
         return None
     rates = {}
-    for m in re.finditer(r"^\|\s*(v_[a-z0-9_]+)\s*\|\s*([0-9.]+)\s*\|", open(path).read(), re.M):
+    text = open(path).read()
+    for m in re.finditer(r"^\|\s*(v_[a-z0-9_]+)\s*\|\s*([0-9.]+)\s*\|", text, re.M):
         rates[m.group(1)] = float(m.group(2))
+    m = re.search(r"^\|\s*lazy forward butterfly \(T butterflies/s\)\s*\|\s*([0-9.]+)\s*\|", text, re.M)
+    if m:
+        rates["butterfly"] = float(m.group(1))
     return rates or None
+
+
+def ntt_roofline(limbs_per_s: float, log_n: int, inverse: bool, rates: dict | None) -> dict:
+    """A limb-NTT rate against both ceilings.  One limb-NTT is (N/2) log N butterflies (the
+    inverse also multiplies every coefficient by N^-1) and reads and writes its N words once."""
+    n = 1 << log_n
+    bfly = n // 2 * log_n
+    slots = bfly * SLOT["bfly"] + (n * SLOT["cmul"] if inverse else 0)
+    nbytes = 2 * n * 4
+    out = {"bound": "alu" if slots / VALU_PEAK >= nbytes / HBM_PEAK else "hbm",
+           "valu_frac": round(limbs_per_s * slots / VALU_PEAK, 4),
+           "hbm_frac": round(limbs_per_s * nbytes / HBM_PEAK, 4),
+           "slots_per_limb": slots, "bytes_per_limb": nbytes}
+    if rates and "butterfly" in rates:
+        # against the measured butterfly throughput, the ceiling of every transform stage
+        out["frac_vs_butterfly_rate"] = round(limbs_per_s * bfly / (rates["butterfly"] * 1e12), 4)
+    return out
 
 
 # ---------------------------------------------------------------- timing
@@ -360,6 +381,10 @@ def headline(args, primes, torch):
     nt1 = interleaved({"forward": lambda i: tiny.ntt_fwd(y, 0), "inverse": lambda i: tiny.ntt_inv(y, 0)},
                       args.steps, args.warmup, 2, torch, items=2 * TINY[1], unit="limb_ntts_per_s")
     tiny.close()
+    rates = read_valu_rates()
+    for st, log_n in ((nt, LOG_N), (nt1, TINY[0])):
+        for d in st:
+            st[d]["roofline"] = ntt_roofline(st[d]["limb_ntts_per_s_at_median"], log_n, d == "inverse", rates)
 
     head = res[head_name]
     wm = work_model(LEVEL, BATCH, head_name == "regen")
@@ -371,7 +396,6 @@ def headline(args, primes, torch):
     # the committed counter summaries were taken on the vector-unit conversion
     traffic = read_traffic(dominant) if args.conv == "vector" else None
     issue = read_issue(dominant) if args.conv == "vector" else None
-    rates = read_valu_rates()
     total_slots = sum(wm.values())
     t_call = head_ms * 1e-3
     roof = {"bound": "alu", "kernel": dominant, "achieved": round(achieved / 1e12, 3),

@@ -98,6 +98,22 @@ def test_instruction_rates_parse():
     rates = bench.read_valu_rates()
     assert rates is not None
     assert 30 < rates["v_mul_lo_u32"] < 45 and 55 < rates["v_add_u32"] < 75
+    assert 3 < rates["butterfly"] < 5
+
+
+def test_ntt_roofline_units():
+    # a forward limb-NTT at N = 2^16: 2^15 * 16 butterflies, 512 KiB read and written once
+    r = bench.ntt_roofline(1e6, 16, False, {"butterfly": 4.0})
+    assert r["slots_per_limb"] == (N // 2) * 16 * bench.SLOT["bfly"]
+    assert r["bytes_per_limb"] == 2 * LIMB
+    assert r["valu_frac"] == pytest.approx(1e6 * r["slots_per_limb"] / bench.VALU_PEAK, abs=1e-4)
+    assert r["hbm_frac"] == pytest.approx(1e6 * 2 * LIMB / 8e12, abs=1e-4)
+    assert r["frac_vs_butterfly_rate"] == pytest.approx(1e6 * (N // 2) * 16 / 4e12, abs=1e-4)
+    assert r["bound"] == "alu"
+    # the inverse also scales by N^-1: one constant multiply per coefficient
+    inv = bench.ntt_roofline(1e6, 16, True, None)
+    assert inv["slots_per_limb"] - r["slots_per_limb"] == N * bench.SLOT["cmul"]
+    assert "frac_vs_butterfly_rate" not in inv
 
 
 def test_source_hash_follows_code_not_comments():
