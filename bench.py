@@ -21,6 +21,12 @@ Output: one JSON line.  Besides the headline it carries the stored-key variant,
 limb-NTTs/s (ring 2^16 batch and the 2^12 ciphertext), workloads 3-5 in both
 variants (unless --no-extra), the roofline of the dominant kernel and the CPU
 oracle timed on a bounded sample of the same workload (unless --no-cpu).
+
+Parity gate.  The oracle switches of that sample (every ciphertext of the batch
+with the stored a-half, one with the regenerated one) are compared bit for bit
+with the timed call's outputs on the same inputs, in both variants; the line
+carries the result under "parity", and a mismatch withholds "value" (null) and
+makes the exit status 1.  With --no-cpu nothing is compared.
 """
 from __future__ import annotations
 
@@ -273,11 +279,13 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "available_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
 
 
-def cpu_baseline(primes, cts, key_b, seed: bytes) -> dict:
+def cpu_baseline(primes, cts, key_b, seed: bytes) -> tuple[dict, list]:
     """The oracle as it stands, on the host's cores, on ciphertexts of the headline workload.
 
     One core: one regenerated-key and one stored-key switch at level 36, and the forward and
-    inverse transform of 36 limbs.  All cores: one stored-key switch per worker process at once."""
+    inverse transform of 36 limbs.  All cores: one stored-key switch per worker process at once.
+    Also returns the oracle's outputs as (ciphertext index, key variant, [2][36][N]) for the
+    parity gate."""
     import numpy as np
 
     from oracle import ks as oks, pool
@@ -290,10 +298,10 @@ def cpu_baseline(primes, cts, key_b, seed: bytes) -> dict:
     kb = np.asarray(key_b, dtype=np.uint64)
     ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
     t0 = time.perf_counter()
-    oks.keyswitch(pr, cts[0].astype(np.uint64), LEVEL, kb, GALOIS, seed=seed)
+    y_regen = oks.keyswitch(pr, cts[0].astype(np.uint64), LEVEL, kb, GALOIS, seed=seed)
     t_regen = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oks.keyswitch(pr, cts[1].astype(np.uint64), LEVEL, kb, GALOIS, key_a=ka)
+    y_stored = oks.keyswitch(pr, cts[1].astype(np.uint64), LEVEL, kb, GALOIS, key_a=ka)
     t_stored = time.perf_counter() - t0
     x = cts[2][0].astype(np.uint64)
     t0 = time.perf_counter()
@@ -307,10 +315,12 @@ def cpu_baseline(primes, cts, key_b, seed: bytes) -> dict:
     try:
         jobs = [(cts[i % len(cts)], LEVEL, GALOIS) for i in range(n_w)]
         t0 = time.perf_counter()
-        pool.run_jobs(ex, jobs)
+        ys = pool.run_jobs(ex, jobs)
         t_all = time.perf_counter() - t0
     finally:
         ex.shutdown()
+    outputs = [(0, "regen", y_regen), (1, "stored", y_stored)]
+    outputs += [(i % len(cts), "stored", y) for i, y in enumerate(ys)]
     return {"value": round(n_w / t_all, 4), "unit": "key-switches/s", "cores": n_w, "kind": "oracle",
             "sample": f"{n_w} ciphertexts of the batch-8, level-36, g=5 workload, one per worker process "
                       f"(stored a-half), switched at once on {n_w} cores in {t_all:.1f} s; one core: one "
@@ -319,7 +329,24 @@ def cpu_baseline(primes, cts, key_b, seed: bytes) -> dict:
             "single_core": {"regen_key_switches_per_s": round(1 / t_regen, 4),
                             "stored_key_switches_per_s": round(1 / t_stored, 4),
                             "ntt_limbs_per_s": {"forward": round(LEVEL / t_fwd, 1), "inverse": round(LEVEL / t_inv, 1)}},
-            "host": host_cpu()}
+            "host": host_cpu()}, outputs
+
+
+def parity_check(gpu_out: dict, oracle_out: list) -> dict:
+    """The timed call's outputs (per key variant, [batch][2][level][N]) against the oracle's outputs
+    for the same ciphertexts.  The regenerated a-half equals the stored one, so every oracle output
+    is compared with the output of every variant."""
+    import numpy as np
+
+    bad, cts = [], set()
+    for ci, how, y in oracle_out:
+        cts.add(int(ci))
+        for v, g in gpu_out.items():
+            if not np.array_equal(np.asarray(g[ci], dtype=np.uint64), np.asarray(y, dtype=np.uint64)):
+                bad.append({"ciphertext": int(ci), "gpu_variant": v, "oracle_key": how})
+    return {"bit_exact": not bad and bool(oracle_out), "ciphertexts": sorted(cts), "variants": sorted(gpu_out),
+            "outputs_compared": len(oracle_out) * len(gpu_out), "mismatches": bad,
+            "against": "the CPU oracle's switches of the cpu_baseline leg (same inputs and key)"}
 
 
 # ---------------------------------------------------------------- headline
@@ -381,6 +408,13 @@ def headline(args, primes, torch):
     nt1 = interleaved({"forward": lambda i: tiny.ntt_fwd(y, 0), "inverse": lambda i: tiny.ntt_inv(y, 0)},
                       args.steps, args.warmup, 2, torch, items=2 * TINY[1], unit="limb_ntts_per_s")
     tiny.close()
+    # the timed call's outputs on the first input copy, per variant, for the parity gate (untimed)
+    gpu_out = {}
+    for v, fn in fns.items():
+        outs[0].zero_()
+        fn(0)
+        torch.cuda.synchronize()
+        gpu_out[v] = outs[0].cpu().numpy().view(np.uint32).copy()
     rates = read_valu_rates()
     for st, log_n in ((nt, LOG_N), (nt1, TINY[0])):
         for d in st:
@@ -437,7 +471,7 @@ def headline(args, primes, torch):
         "key_bytes": {"stored": 2 * DNUM * (L + K) * N * 4, "regen": DNUM * (L + K) * N * 4 + 32},
     }
     ctx.close()
-    return out, {"cts": cts, "key_b": kb_host, "seed": seed}
+    return out, {"cts": cts, "key_b": kb_host, "seed": seed, "gpu_out": gpu_out}
 
 
 def synth_chain(t) -> list[int]:
@@ -698,11 +732,22 @@ def main() -> int:
             r = run_workload(w, args, primes, torch)
             print(f"[bench] workload {w} done", file=sys.stderr, flush=True)
             out["workloads"][str(w)] = {k: v for k, v in r.items() if k not in ("n_gpus", "dtype", "data")}
+    out["parity"] = {"bit_exact": None, "reason": "--no-cpu: the oracle did not run"}
     if not args.no_cpu:
         try:
-            out["cpu_baseline"] = cpu_baseline(primes, host_inputs["cts"], host_inputs["key_b"], host_inputs["seed"])
+            out["cpu_baseline"], oracle_out = cpu_baseline(primes, host_inputs["cts"], host_inputs["key_b"],
+                                                           host_inputs["seed"])
+            out["parity"] = parity_check(host_inputs["gpu_out"], oracle_out)
         except Exception as e:  # the GPU line stands on its own; say why the baseline is missing
             out["cpu_baseline"] = {"value": None, "unit": "key-switches/s", "kind": "oracle", "error": repr(e)}
+            out["parity"] = {"bit_exact": None, "reason": f"the oracle failed: {e!r}"}
+    if out["parity"]["bit_exact"] is False:
+        # no throughput is reported for a path that computes something else
+        print(f"bench.py: the timed key-switch differs from the oracle: {out['parity']['mismatches']}",
+              file=sys.stderr)
+        out["value"] = None
+        print(json.dumps(out))
+        return 1
     print(json.dumps(out))
     return 0
 

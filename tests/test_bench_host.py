@@ -125,3 +125,20 @@ def test_source_hash_follows_code_not_comments():
     assert bench.kernel_source_hash(commented) == h
     changed = [texts[0] + "\nstatic int extra_symbol;", texts[1], texts[2]]
     assert bench.kernel_source_hash(changed) != h
+
+
+def test_parity_gate_compares_every_oracle_output_with_every_variant():
+    import numpy as np
+
+    rng = np.random.default_rng(7)
+    gpu = rng.integers(0, 2**32, (3, 2, 2, 8), dtype=np.uint64).astype(np.uint32)
+    gpu_out = {"regen": gpu.copy(), "stored": gpu.copy()}
+    oracle = [(0, "regen", gpu[0].astype(np.uint64)), (2, "stored", gpu[2].astype(np.uint64)),
+              (0, "stored", gpu[0].astype(np.uint64))]
+    p = bench.parity_check(gpu_out, oracle)
+    assert p["bit_exact"] is True and p["ciphertexts"] == [0, 2] and p["outputs_compared"] == 6
+    gpu_out["stored"][2, 1, 0, 5] ^= 1  # one residue of one variant
+    p = bench.parity_check(gpu_out, oracle)
+    assert p["bit_exact"] is False
+    assert p["mismatches"] == [{"ciphertext": 2, "gpu_variant": "stored", "oracle_key": "stored"}]
+    assert bench.parity_check(gpu_out, [])["bit_exact"] is False  # nothing compared proves nothing
