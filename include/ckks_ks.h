@@ -58,6 +58,13 @@ typedef enum {
 /* Thread-local description of the last failure on the calling thread ("" if none). */
 const char *ckks_last_error(void);
 
+/* Build identity, for callers that must not run a stale library: the first 16
+ * hex digits of the sha256 of the sources the library was compiled from (the
+ * kernel, host and header files, by name and content), fixed at build time.  The
+ * Python binding compares it with the sources beside it and refuses a mismatch.
+ * A static string; never fails. */
+const char *ckks_build_id(void);
+
 /* The `count` largest primes q < 2^bits with q = 1 mod 2^(log_n+1), in descending
  * order, written to out_host[0..count) (host).  This is the chain reading used
  * throughout: the pages fix only "a 32-bit RNS CKKS chain".  bits in 20..32. */

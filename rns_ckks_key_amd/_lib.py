@@ -1,7 +1,8 @@
 """ctypes binding of libckks_ks.so (argument marshalling only; every step runs in the HIP library).
 
 The shared object is built in-tree by `python -m rns_ckks_key_amd.build`.  If
-it is missing, importing this module raises: there is no fallback path.
+it is missing, or was built from other sources than the ones beside it,
+importing this module raises: there is no fallback path.
 """
 from __future__ import annotations
 
@@ -55,6 +56,7 @@ class KsItem(ctypes.Structure):
 
 
 _SIGS = {
+    "ckks_build_id": (ctypes.c_char_p, []),
     "ckks_last_error": (ctypes.c_char_p, []),
     "ckks_chain_primes": (ctypes.c_int, [U32, U32, U32, PU32]),
     "ckks_ctx_create": (ctypes.c_int, [ctypes.POINTER(PCTX), U32, U32, U32, U32, PU32, U32]),
@@ -88,6 +90,20 @@ for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
     _f.restype = _res
     _f.argtypes = _args
+
+
+def _check_build() -> None:
+    """Refuse a library built from other sources than the ones beside it (a stale build)."""
+    from rns_ckks_key_amd.build import source_digest
+
+    built, now = lib.ckks_build_id().decode(), source_digest()
+    if built != now:
+        raise ImportError(f"{LIB_PATH} was built from other sources (digest {built}) than those in "
+                          f"rns_ckks_key_amd/csrc and include/ ({now}); rebuild with "
+                          f"`python -m rns_ckks_key_amd.build`")
+
+
+_check_build()
 
 
 def header_functions() -> list[str]:

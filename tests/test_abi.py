@@ -233,3 +233,24 @@ def test_noalloc_keyswitch_validates_before_any_launch():
     assert nk(out=ct) == EINVAL and "overlaps ct" in lib.ckks_last_error().decode()
     assert nk() == EINVAL and "host-only" in lib.ckks_last_error().decode()
     boot.close()
+
+
+def test_library_is_built_from_the_sources_beside_it(monkeypatch, tmp_path):
+    from rns_ckks_key_amd import build
+
+    assert lib.ckks_build_id().decode() == build.source_digest()
+    # the digest follows the content of every source and header
+    copies = []
+    for path in [build.os.path.join(build.CSRC, s) for s in build.SOURCES] + build.HEADERS:
+        c = tmp_path / build.os.path.basename(path)
+        c.write_bytes(open(path, "rb").read())
+        copies.append(c)
+    monkeypatch.setattr(build, "CSRC", str(tmp_path))
+    monkeypatch.setattr(build, "HEADERS", [str(c) for c in copies[len(build.SOURCES):]])
+    same = build.source_digest()
+    assert same == lib.ckks_build_id().decode()
+    copies[0].write_bytes(copies[0].read_bytes() + b"\n")
+    assert build.source_digest() != same
+    # a library built from other sources is refused at import
+    with pytest.raises(ImportError, match="rebuild"):
+        _lib._check_build()
