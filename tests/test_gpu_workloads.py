@@ -1,9 +1,10 @@
 """GPU parity on the shapes of the level sweep, the hoisted 16-key stage and the mixed decode stream.
 
 Each run executes the whole workload on the GPU in the launch configuration the
-benchmark times; sampled outputs are compared bit-exactly with the oracle.  Key
-b-halves are uniform residues (the same distribution as a real b-half): the bits
-of the output do not depend on whether the key is a valid encryption.
+benchmark times, and every output is compared bit-exactly with the oracle (run
+on the host's cores by tests/oracle_jobs.py).  Key b-halves are uniform residues
+(the same distribution as a real b-half): the bits of the output do not depend
+on whether the key is a valid encryption.
 """
 import functools
 import hashlib
@@ -14,7 +15,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_common import CHAINS, announce, context, first_mismatch, gpu, host, params
-from oracle.pool import keyswitch_many
+from tests.oracle_jobs import switch_all
 
 pytestmark = pytest.mark.gpu
 
@@ -37,55 +38,50 @@ def key_a(seed: bytes):
     return expand_key_a(seed, pr.primes, pr.dnum, pr.n)
 
 
-SWEEP_SAMPLE = {36: 15, 24: 7, 12: 0, 4: 9}   # ciphertext of each level's batch checked against the oracle
-HOIST_SAMPLE = (0, 9, 15)                      # keys of the hoisted stage checked against the oracle
-
-
 @functools.lru_cache(maxsize=None)
 def _sweep_oracle():
+    # all 64 ciphertexts of the sweep (16 at each level) under workload 2's key
     pr = params("boot")
     d = synth.draw(3, pr.primes)
     seed = d.keys[0].seed
-    jobs = []
-    for li, level in enumerate(synth.WORKLOADS[3].levels):
-        jobs.append((d.cts[16 * li + SWEEP_SAMPLE[level]], level, 5))
-    want = keyswitch_many(CHAINS["boot"], key_rows(3003), key_a(seed), jobs)
-    return dict(zip(synth.WORKLOADS[3].levels, want))
+    jobs = [(ct, lvl, 5, 3003, seed) for ct, lvl in zip(d.cts, d.levels)]
+    return switch_all(CHAINS["boot"], jobs)
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
 def test_level_sweep_batch16(variant):
-    # workload 3: batch 16 at levels 36, 24, 12, 4 under workload 2's key; one ciphertext per
-    # level against the oracle, with the a-half regenerated or stored
+    # workload 3: batch 16 at levels 36, 24, 12, 4 under workload 2's key, with the a-half
+    # regenerated or stored; every ciphertext of every level against the oracle
     pr = params("boot")
     ctx = context("boot", 16)
     d = synth.draw(3, pr.primes)
     seed = d.keys[0].seed
     dkb = gpu(key_rows(3003))
     dka = gpu(key_a(seed)) if variant == "stored" else None
+    announce(f"level sweep oracle (64 switches) {variant}")
     want = _sweep_oracle()
     for li, level in enumerate(synth.WORKLOADS[3].levels):
         announce(f"level sweep level={level} {variant}")
         cts = np.stack(d.cts[16 * li:16 * li + 16])
         got = host(ctx.keyswitch(gpu(cts), level, dkb, 5, key_seed=seed if dka is None else None, key_a=dka))
-        b = SWEEP_SAMPLE[level]
-        assert np.array_equal(got[b], want[level]), (level, b, first_mismatch(got[b], want[level]))
+        for b in range(16):
+            w = want[16 * li + b]
+            assert np.array_equal(got[b], w), (level, b, first_mismatch(got[b], w))
 
 
 @functools.lru_cache(maxsize=None)
 def _hoist_oracle():
+    # the ciphertext under each of the 16 keys
     pr = params("boot")
     d = synth.draw(4, pr.primes)
-    kbs = [key_rows(4000 + k) for k in HOIST_SAMPLE]
-    kas = [key_a(d.keys[k].seed) for k in HOIST_SAMPLE]
-    jobs = [(d.cts[0], 36, d.keys[k].galois, i) for i, k in enumerate(HOIST_SAMPLE)]
-    return dict(zip(HOIST_SAMPLE, keyswitch_many(CHAINS["boot"], kbs, kas, jobs)))
+    jobs = [(d.cts[0], 36, kd.galois, 4000 + k, kd.seed) for k, kd in enumerate(d.keys)]
+    return switch_all(CHAINS["boot"], jobs)
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
 def test_hoisted_sixteen_keys(variant):
     # workload 4: one ciphertext at level 36, 16 keys g = 5^k with their own seeds (or their
-    # stored a-halves), one hoisted call; three keys against the oracle
+    # stored a-halves), one hoisted call; every key's output against the oracle
     announce(f"hoisted 16 keys {variant}")
     pr = params("boot")
     ctx = context("boot", 16)
@@ -96,7 +92,8 @@ def test_hoisted_sixteen_keys(variant):
         ka = gpu(key_a(kd.seed)) if variant == "stored" else None
         keys.append((gpu(key_rows(4000 + k)), kd.galois, kd.seed if ka is None else None, ka))
     got = host(ctx.keyswitch_hoisted(gpu(ct), 36, keys))
-    for k, want in _hoist_oracle().items():
+    announce(f"hoisted oracle (16 switches) {variant}")
+    for k, want in enumerate(_hoist_oracle()):
         assert np.array_equal(got[k], want), (k, first_mismatch(got[k], want))
 
 
@@ -141,8 +138,20 @@ def test_tiny_workload_exact_draw(variant):
     assert np.array_equal(host(t2), want_i), first_mismatch(host(t2), want_i)
 
 
+@functools.lru_cache(maxsize=None)
+def _mixed_oracle():
+    # each of the 64 ciphertexts under its key
+    pr = params("boot")
+    d = synth.draw(5, pr.primes)
+    wl = synth.WORKLOADS[5]
+    jobs = [(ct, d.levels[i], wl.galois[d.key_index[i]], 5000 + d.key_index[i], d.keys[d.key_index[i]].seed)
+            for i, ct in enumerate(d.cts)]
+    return switch_all(CHAINS["boot"], jobs)
+
+
 def test_mixed_stream_sixty_four():
-    # workload 5: 64 ciphertexts, levels 8..36, each under one of 33 keys; one call per ciphertext
+    # workload 5: 64 ciphertexts, levels 8..36, each under one of 33 keys; one call per
+    # ciphertext; every output against the oracle
     announce("mixed stream 64")
     pr = params("boot")
     ctx = context("boot", 16)
@@ -156,18 +165,15 @@ def test_mixed_stream_sixty_four():
             dkb[k] = gpu(key_rows(5000 + k))
         lvl = d.levels[i]
         outs.append(ctx.keyswitch(gpu(ct[None]), lvl, dkb[k], wl.galois[k], key_seed=d.keys[k].seed))
-    sample = (0, 31, 63)
-    ks = sorted({d.key_index[i] for i in sample})
-    jobs = [(d.cts[i], d.levels[i], wl.galois[d.key_index[i]], ks.index(d.key_index[i])) for i in sample]
-    wants = keyswitch_many(CHAINS["boot"], [key_rows(5000 + k) for k in ks], [key_a(d.keys[k].seed) for k in ks], jobs)
-    for i, want in zip(sample, wants):
+    announce("mixed stream oracle (64 switches)")
+    for i, want in enumerate(_mixed_oracle()):
         got = host(outs[i])[0]
         assert np.array_equal(got, want), (i, d.levels[i], d.key_index[i], first_mismatch(got, want))
 
 
 def test_multi_item_equals_single_calls():
     # ckks_keyswitch_multi over the mixed stream (levels repeat, keys differ, stored and regenerated mixed)
-    # is bit-identical to one ckks_keyswitch call per item; two items are checked against the oracle
+    # is bit-identical to one ckks_keyswitch call per item, and every item equals the oracle
     announce("multi-item stream")
     pr = params("boot")
     ctx = context("boot", 16)
@@ -189,9 +195,5 @@ def test_multi_item_equals_single_calls():
         single = ctx.keyswitch(ct[None], lvl, kb, g, key_seed=seed, key_a=ka)
         a, b = host(outs[i]), host(single)[0]
         assert np.array_equal(a, b), (i, lvl, first_mismatch(a, b))
-    sample = (5, 40)
-    ks = sorted({d.key_index[i] for i in sample})
-    jobs = [(d.cts[i], d.levels[i], wl.galois[d.key_index[i]], ks.index(d.key_index[i])) for i in sample]
-    wants = keyswitch_many(CHAINS["boot"], [key_rows(5000 + k) for k in ks], [key_a(d.keys[k].seed) for k in ks], jobs)
-    for i, want in zip(sample, wants):
+    for i, want in enumerate(_mixed_oracle()):
         assert np.array_equal(host(outs[i]), want), (i, first_mismatch(host(outs[i]), want))

@@ -24,3 +24,23 @@ def test_pool_equals_direct_oracle_calls():
     one = keyswitch_many(chain, kbs[1], kas[1], [(cts[0], 4, 125)])
     assert np.array_equal(one[0], oks.keyswitch(pr, cts[0].astype(np.uint64), 4, kbs[1].astype(np.uint64), 125,
                                                 key_a=kas[1]))
+
+
+def test_workload_runner_builds_each_key_in_its_worker():
+    # tests/oracle_jobs.switch_all: a job names its key by seeds and the worker builds it; the
+    # outputs equal direct oracle calls with the keys built here, with the regenerated a-half
+    # (seed=) as the reference, so the runner's stored expansion is checked against it too
+    from tests.oracle_jobs import switch_all
+
+    chain = (12, 4, 2, 2, 30)
+    pr = Params.make(*chain)
+    rng = np.random.default_rng(56)
+    seeds = [rng.bytes(32) for _ in range(2)]
+    cts = [np.stack([synth.residues(rng, pr.primes[:lv], pr.n) for _ in range(2)]) for lv in (4, 2, 3, 4)]
+    jobs = [(cts[0], 4, 5, 70, seeds[0]), (cts[1], 2, 25, 71, seeds[1]), (cts[2], 3, 1, 70, seeds[0]),
+            (cts[3], 4, 8191, 71, seeds[1])]
+    got = switch_all(chain, jobs, max_workers=2)
+    for (ct, lv, g, kbs, sd), out in zip(jobs, got):
+        kb = synth.uniform_key_rows(kbs, pr.primes, pr.dnum, pr.n).astype(np.uint64)
+        want = oks.keyswitch(pr, ct.astype(np.uint64), lv, kb, g, seed=sd)
+        assert np.array_equal(out, want)
