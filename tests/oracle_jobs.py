@@ -51,3 +51,33 @@ def switch_all(chain: tuple, jobs: list[tuple], max_workers: int | None = None) 
             for ct, level, g, kbs, a in jobs]
     with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
         return list(ex.map(_switch, args, timeout=900.0))
+
+
+_KEY: dict = {}
+
+
+def _init_key(chain: tuple, kb: np.ndarray, ka: np.ndarray) -> None:
+    _KEY["pr"] = _params(chain)
+    _KEY["key"] = (kb.astype(np.uint64), ka.astype(np.uint64))
+
+
+def _mul_relin_rescale(job: tuple) -> np.ndarray:
+    from oracle import mult
+
+    x, y, level = job
+    kb, ka = _KEY["key"]
+    return mult.mul_relin_rescale(_KEY["pr"], x.astype(np.uint64), y.astype(np.uint64), level, kb, key_a=ka)
+
+
+def mul_relin_rescale_all(chain: tuple, kb, ka, jobs: list[tuple], max_workers: int | None = None) -> list[np.ndarray]:
+    """Oracle multiply-relinearise-rescale of each job (x, y [2][level][N], level) under one
+    relinearisation key (kb, ka [dnum][L+K][N]), given to each worker once; outputs in job order."""
+    from oracle.pool import workers
+
+    n = max(1, min(len(jobs), max_workers or workers(16)))
+    key = (np.ascontiguousarray(kb, dtype=np.uint32), np.ascontiguousarray(ka, dtype=np.uint32))
+    args = [(np.ascontiguousarray(x, dtype=np.uint32), np.ascontiguousarray(y, dtype=np.uint32), int(level))
+            for x, y, level in jobs]
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=_init_key,
+                             initargs=(chain, *key)) as ex:
+        return list(ex.map(_mul_relin_rescale, args, timeout=900.0))

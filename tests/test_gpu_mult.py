@@ -3,15 +3,17 @@
 Covers every level of the N=2^12 chain, batches that take each inner-product
 kernel shape (1, 5 and 8 ciphertexts), regenerated and stored key halves, the
 multiply-by-one identity, the decryption of an encrypted product, the
-bootstrapping-scale configuration (batch 8 at level 36, two ciphertexts against
-the oracle) and the argument errors.
+bootstrapping-scale configuration (batch 8 at level 36, every product against
+the oracle, run on the host's cores by tests/oracle_jobs.py) and the argument
+errors.
 """
 import functools
 
 import numpy as np
 import pytest
 
-from tests.gpu_common import announce, context, first_mismatch, gpu, host, params, rand_limbs, torch
+from tests.gpu_common import CHAINS, announce, context, first_mismatch, gpu, host, params, rand_limbs, torch
+from tests.oracle_jobs import mul_relin_rescale_all
 
 pytestmark = pytest.mark.gpu
 
@@ -102,9 +104,18 @@ def test_mul_by_one_is_rescale_and_product_decrypts():
     assert worst < oks.noise_bound(pr, level) / ql + pr.n + 2, worst
 
 
+@functools.lru_cache(maxsize=None)
+def _batch8_oracle():
+    pr = params("boot")
+    kb, ka, seed, s = relin_key("boot")
+    rng = np.random.default_rng(12)
+    x, y = _ct(rng, pr, 36, 8), _ct(rng, pr, 36, 8)
+    return mul_relin_rescale_all(CHAINS["boot"], kb, ka, [(x[b], y[b], 36) for b in range(8)])
+
+
 @pytest.mark.parametrize("variant", ["regen", "stored"])
-def test_mul_relin_rescale_boot_batch8_sampled(variant):
-    # batch 8 at level 36 (the bootstrapping-scale chain); ciphertexts 0 and 7 against the oracle
+def test_mul_relin_rescale_boot_batch8(variant):
+    # batch 8 at level 36 (the bootstrapping-scale chain); every product against the oracle
     announce(f"mul_relin_rescale boot batch 8 {variant}")
     pr = params("boot")
     ctx = context("boot", 8)
@@ -113,8 +124,7 @@ def test_mul_relin_rescale_boot_batch8_sampled(variant):
     x, y = _ct(rng, pr, 36, 8), _ct(rng, pr, 36, 8)
     got = host(ctx.mul_relin_rescale(gpu(x), gpu(y), 36, gpu(kb), key_seed=seed if variant == "regen" else None,
                                      key_a=gpu(ka) if variant == "stored" else None))
-    for b in (0, 7):
-        want = omult.mul_relin_rescale(pr, x[b], y[b], 36, kb, key_a=ka)
+    for b, want in enumerate(_batch8_oracle()):
         assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
 
 

@@ -44,3 +44,25 @@ def test_workload_runner_builds_each_key_in_its_worker():
         kb = synth.uniform_key_rows(kbs, pr.primes, pr.dnum, pr.n).astype(np.uint64)
         want = oks.keyswitch(pr, ct.astype(np.uint64), lv, kb, g, seed=sd)
         assert np.array_equal(out, want)
+
+
+def test_multiply_runner_equals_direct_oracle_calls():
+    # tests/oracle_jobs.mul_relin_rescale_all: the relinearisation key goes to each worker once
+    from oracle import mult as omult
+    from tests.oracle_jobs import mul_relin_rescale_all
+
+    chain = (12, 4, 2, 2, 30)
+    pr = Params.make(*chain)
+    rng = np.random.default_rng(57)
+    s = synth.ternary(rng, pr.n)
+    kb, ka = omult.relin_keygen(pr, s, [synth.gaussian(rng, pr.n) for _ in range(pr.dnum)], rng.bytes(32))
+
+    def ct(lv):
+        return np.stack([synth.residues(rng, pr.primes[:lv], pr.n) for _ in range(2)])
+
+    jobs = [(ct(4), ct(4), 4), (ct(2), ct(2), 2), (ct(3), ct(3), 3)]
+    got = mul_relin_rescale_all(chain, kb, ka, jobs, max_workers=2)
+    for (x, y, lv), out in zip(jobs, got):
+        want = omult.mul_relin_rescale(pr, x.astype(np.uint64), y.astype(np.uint64), lv, kb.astype(np.uint64),
+                                       key_a=ka.astype(np.uint64))
+        assert np.array_equal(out, want)
