@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_common import announce, first_mismatch, gpu, host, rand_limbs, torch
+from oracle.pool import keyswitch_many
 
 pytestmark = pytest.mark.gpu
 
@@ -173,9 +174,9 @@ def test_keyswitch_batches_eight_digits(batch):
 
 
 @pytest.mark.parametrize("variant", ["regen", "stored"])
-def test_smaller_ring_workload_sampled(variant):
+def test_smaller_ring_workload(variant):
     # the smaller-ring benchmark configuration: N=2^15, 20+7 primes of 32 bits, dnum 3,
-    # batch 8 at level 20, g = 5; ciphertexts 0 and 7 against the oracle
+    # batch 8 at level 20, g = 5; every ciphertext against the oracle
     announce(f"smaller ring batch 8 level 20 {variant}")
     shape = (15, 20, 7, 3, 32)
     pr = Params.make(*shape)
@@ -187,8 +188,8 @@ def test_smaller_ring_workload_sampled(variant):
     ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
     got = host(ctx.keyswitch(gpu(ct), 20, gpu(kb), 5, key_seed=seed if variant == "regen" else None,
                              key_a=gpu(ka) if variant == "stored" else None))
-    for b in (0, 7):
-        want = oks.keyswitch(pr, ct[b], 20, kb, 5, key_a=ka)
+    wants = keyswitch_many(shape, kb, ka, [(ct[b], 20, 5) for b in range(8)])
+    for b, want in enumerate(wants):
         assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
     ctx.close()
 
@@ -198,7 +199,7 @@ def test_wide_conversion_workgroups_other_rings(shape):
     # batch 8 at level 36: both conversions have 36 targets x 16 columns per
     # workgroup and take 512-thread workgroups; ring 2^15 (32-bit primes: lazy
     # column butterflies; 31-bit: canonical) and ring 2^16 with 31-bit primes cover
-    # the instantiations the main chain does not; ciphertexts 0 and 7 against the oracle
+    # the instantiations the main chain does not; every ciphertext against the oracle
     announce(f"wide conversion shape {shape} batch 8 level 36")
     pr = Params.make(*shape)
     ctx = Context(shape[0], shape[1], shape[2], shape[3], pr.primes, 8)
@@ -208,7 +209,7 @@ def test_wide_conversion_workgroups_other_rings(shape):
     seed = rng.bytes(32)
     ka = expand_key_a(seed, pr.primes, pr.dnum, pr.n)
     got = host(ctx.keyswitch(gpu(ct), 36, gpu(kb), 25, key_seed=seed))
-    for b in (0, 7):
-        want = oks.keyswitch(pr, ct[b], 36, kb, 25, key_a=ka)
+    wants = keyswitch_many(shape, kb, ka, [(ct[b], 36, 25) for b in range(8)])
+    for b, want in enumerate(wants):
         assert np.array_equal(got[b], want), (b, first_mismatch(got[b], want))
     ctx.close()
