@@ -45,8 +45,7 @@ def test_ntt_full_ciphertext_batch_of_eight():
     t = gpu(a)
     ctx.ntt_fwd(t, 0)
     got = host(t)
-    for b in (0, 15):
-        want = ntt(a[b, ::7], pr.primes[:36:7], pr.psis[:36:7])
-        assert np.array_equal(got[b, ::7], want), first_mismatch(got[b, ::7], want)
+    want = ntt(a, pr.primes[:36], pr.psis[:36])  # every limb of every item
+    assert np.array_equal(got, want), first_mismatch(got, want)
     ctx.ntt_inv(t, 0)
     assert np.array_equal(host(t), a)
